@@ -1,0 +1,237 @@
+/*
+ * pqhsa.h -- C ABI of libpqhsa: one decode step of PQ-HSA attention on an
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (rit.work blog, "PQ-HSA long-context attention", section "How
+ * approximate estimates return the discarded context"): every KV head's keys
+ * are indexed with IVF-PQ (clusters plus compressed codes); each indexed
+ * token gets an approximate attention logit from the index; a budget of the
+ * best tokens, the first tokens, the recent window and the not-yet-indexed
+ * tail are attended exactly from the paged KV cache; every other token stays
+ * in the softmax through its approximate weight, and its numerator is that
+ * weight summed per cluster times the cluster's mean value:
+ *     O = (N_exact + N_bg) / (D_exact + D_bg).
+ * The last identity is the prefix/suffix merge of the quant_prune_distill
+ * post on query reuse (opening paragraph), applied to more than two parts.
+ *
+ * Conventions shared by every entry point
+ *   - Every array pointer is a DEVICE pointer (hipMalloc'd or a torch CUDA
+ *     tensor), owned by the caller.  The library never allocates, frees or
+ *     synchronises; scratch memory comes in through `workspace`.
+ *   - Work is enqueued on `stream`; results are ready when the stream is.
+ *   - Arguments are validated on the host before anything is launched; an
+ *     invalid call returns a status and enqueues nothing.  PQHSA_ERR_HIP means
+ *     a launch failed.  Faults inside kernels surface at the caller's next
+ *     synchronisation.
+ *   - Values that live on the device (context lengths, n_indexed, block
+ *     table entries) are range-checked inside the kernels: out-of-range
+ *     values are clamped so that no access leaves its buffer, and the output
+ *     is then unspecified.  Documented preconditions below say what is valid.
+ *   - bf16 data are passed as uint16_t bit patterns.
+ *   - No global state: concurrent calls on different streams with disjoint
+ *     workspaces are safe.  Calls sharing a workspace must be ordered.
+ *
+ * Supported shapes: head_dim 128, page_size 16, pq_m 16 (8-dim subspaces),
+ * pq_ksub 256, G = num_q_heads / num_kv_heads in {1, 2, 4, 8},
+ * 1 <= num_lists <= 16384.  Query head i uses KV head i / G.
+ */
+#ifndef PQHSA_H
+#define PQHSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pqhsa_status {
+  PQHSA_OK = 0,
+  PQHSA_ERR_INVALID_ARG = 1,     /* null pointer, inconsistent or out-of-range shape field */
+  PQHSA_ERR_UNSUPPORTED = 2,     /* a valid shape these kernels are not built for */
+  PQHSA_ERR_BUFFER_TOO_SMALL = 3,/* index_buf or workspace smaller than the query functions say */
+  PQHSA_ERR_HIP = 4              /* a HIP launch or copy failed */
+} pqhsa_status;
+
+/* Shape and method parameters.  All fields are host values. */
+typedef struct pqhsa_shape {
+  int32_t batch;              /* B >= 1 sequences */
+  int32_t num_q_heads;        /* Hq */
+  int32_t num_kv_heads;       /* Hkv, Hq % Hkv == 0 */
+  int32_t head_dim;           /* 128 */
+  int32_t page_size;          /* tokens per cache page, 16 */
+  int32_t num_pages;          /* pages in each of the K and V caches */
+  int32_t max_pages_per_seq;  /* columns of the block table */
+  int32_t num_lists;          /* L, IVF clusters per (sequence, KV head) */
+  int32_t pq_m;               /* PQ subspaces, 16 */
+  int32_t pq_ksub;            /* codewords per subspace, 256 */
+  int32_t max_context;        /* bound on every context length and index capacity;
+                                 <= max_pages_per_seq * page_size */
+  int32_t n_sink;             /* first tokens always attended exactly, >= 0 */
+  int32_t n_recent;           /* last tokens always attended exactly, >= 0 */
+  int32_t budget_bp;          /* top-k budget in basis points of the context, 0..10000 */
+  float scale;                /* logit scale, normally 1/sqrt(head_dim); > 0 */
+} pqhsa_shape;
+
+/* Number of entry points computed per step (exact partial splits etc.) are
+ * chosen by the library from the shape; these report the buffer sizes. */
+
+/* Bytes of the index buffer for `shape` (0 if the shape is invalid). */
+size_t pqhsa_index_bytes(const pqhsa_shape* shape);
+
+/* Bytes of scratch workspace for pqhsa_upload_index (0 if invalid). */
+size_t pqhsa_upload_workspace_bytes(const pqhsa_shape* shape);
+
+/* Bytes of scratch workspace for one decode step; dense != 0 sizes it for
+ * pqhsa_dense_decode_step instead.  0 if the shape is invalid. */
+size_t pqhsa_workspace_bytes(const pqhsa_shape* shape, int dense);
+
+/* Capacity of the optional `selected` output per (sequence, KV head):
+ * min(ceil(max_context * budget_bp / 10000), max_context). */
+int32_t pqhsa_max_selected(const pqhsa_shape* shape);
+
+/*
+ * Build the per-step index from an IVF-PQ index built after prefill
+ * (PQ-HSA page, section "How approximate estimates return the discarded
+ * context", sixth paragraph: the index is built after the prompt is filled,
+ * newer tokens stay outside it).  Not part of the per-step path.
+ *
+ *   centroids   float [B][Hkv][L][128]          IVF cluster centres
+ *   codebooks   float [B][Hkv][16][256][8]      PQ codewords, shared by the L lists
+ *   list_ids    int32 [B][Hkv][max_context]     cluster of token t (first n_indexed used)
+ *   codes       uint8 [B][Hkv][max_context][16] PQ code of token t's key
+ *   n_indexed   int32 [B]                       indexed prefix length of each sequence;
+ *                                               must be <= max_context
+ *   v_cache     bf16  [num_pages][16][Hkv][128] paged values (for the cluster means)
+ *   block_table int32 [B][max_pages_per_seq]    logical page -> physical page
+ *
+ * Writes into index_buf: the centroids and codebooks, the codes regrouped
+ * by cluster (stable: token order kept inside a cluster) with each entry's
+ * token position, and each cluster's mean value vector over its indexed
+ * tokens (section A, fifth paragraph: the group's mean value; 0 for an
+ * empty cluster).  Tokens whose list id lies outside [0, L) are left out of
+ * the index and counted; pqhsa_index_dropped() reports the count.
+ * index_buf must stay alive and unchanged while decode steps use it.
+ */
+pqhsa_status pqhsa_upload_index(const pqhsa_shape* shape, const float* centroids,
+                                const float* codebooks, const int32_t* list_ids,
+                                const uint8_t* codes, const int32_t* n_indexed,
+                                const uint16_t* v_cache, const int32_t* block_table,
+                                void* index_buf, size_t index_bytes, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* Copy the count of dropped (out-of-range list id) tokens of an uploaded
+ * index to *dropped.  Synchronises `stream`; meant for tests and tooling. */
+pqhsa_status pqhsa_index_dropped(const pqhsa_shape* shape, const void* index_buf,
+                                 int64_t* dropped, hipStream_t stream);
+
+/*
+ * One PQ-HSA decode step for every (sequence, query head).
+ *
+ *   q            bf16  [B][Hq][128]                 current queries
+ *   k_cache      bf16  [num_pages][16][Hkv][128]    paged keys (vLLM layout)
+ *   v_cache      bf16  [num_pages][16][Hkv][128]    paged values
+ *   block_table  int32 [B][max_pages_per_seq]
+ *   context_lens int32 [B]    T_b, 1..max_context, >= n_indexed of the index
+ *   out          float [B][Hq][128]                 attention output O
+ *   selected     int32 [B][Hkv][pqhsa_max_selected] optional (may be NULL):
+ *                the top-k positions in ascending order, -1 padded
+ *   lse          float [B][Hq]                      optional (may be NULL):
+ *                natural log of the full softmax denominator, m + log(D)
+ *
+ * Per (sequence b, KV head h), with T = T_b and n_tail = T - n_indexed:
+ *   forced F  = [0, n_sink) U [T - max(n_recent, n_tail), T)
+ *   candidates C = indexed tokens not in F
+ *   s_hat_g,t = scale * (q_g . C[list_t] + sum_m q_g^(m) . B_m[code_t,m])
+ *   key_t     = max over the G query heads g of s_hat_g,t
+ *   S         = the k = min(ceil(T*budget_bp/10000), |C|) candidates with the
+ *               largest key, ties to the lower position
+ *   exact logits for F U S from the paged cache; for every other candidate
+ *   the weight exp(s_hat - m) is summed per cluster and multiplied by the
+ *   cluster's mean value; one shared normalisation gives O.
+ * (Section A of the PQ-HSA page, paragraphs three to six.  Taking the max
+ * over the group's query heads, the overlap of the recent window with the
+ * tail, and the tie rule are readings where the page is silent.)
+ */
+pqhsa_status pqhsa_decode_step(const pqhsa_shape* shape, const void* index_buf,
+                               const uint16_t* q, const uint16_t* k_cache,
+                               const uint16_t* v_cache, const int32_t* block_table,
+                               const int32_t* context_lens, float* out, int32_t* selected,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * Dense split-K decode attention over each sequence's whole context, through
+ * the same exact-attention and merge kernels as pqhsa_decode_step.  This is
+ * the honest baseline: the activation/KV-sparsity crossover article
+ * (rit.work blog, section "Why one method gives different speed-ups") runs
+ * dense and sparse modes through one split-K kernel, because a slower dense
+ * kernel inflates the measured speed-up.  index_buf is not needed.
+ * Arguments as in pqhsa_decode_step; budget, sink, recent and list fields of
+ * the shape are ignored.
+ */
+pqhsa_status pqhsa_dense_decode_step(const pqhsa_shape* shape, const uint16_t* q,
+                                     const uint16_t* k_cache, const uint16_t* v_cache,
+                                     const int32_t* block_table, const int32_t* context_lens,
+                                     float* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/* Stages of pqhsa_decode_step, in launch order, for profiling. */
+enum {
+  PQHSA_STAGE_TABLES = 0,     /* per-query lookup tables */
+  PQHSA_STAGE_SCAN = 1,       /* code scan: approximate logits, keys, cluster bins */
+  PQHSA_STAGE_COLLECT = 2,    /* top-k: threshold bucket and collection */
+  PQHSA_STAGE_SELECT = 3,     /* top-k: exact threshold, ascending row list */
+  PQHSA_STAGE_EXACT = 4,      /* paged split-K exact attention + background */
+  PQHSA_STAGE_MERGE = 5,      /* log-sum-exp merge into O */
+  PQHSA_NUM_STAGES = 6
+};
+
+/* pqhsa_decode_step that also records stage_events[i] on `stream` right
+ * before stage i is launched and stage_events[PQHSA_NUM_STAGES] after the last
+ * one (PQHSA_NUM_STAGES + 1 events created by the caller).  With dense != 0
+ * it runs pqhsa_dense_decode_step and records events 0 (before the split-K
+ * kernel), 1 (before the merge) and 2 (after it). */
+pqhsa_status pqhsa_decode_step_profiled(const pqhsa_shape* shape, const void* index_buf,
+                                        const uint16_t* q, const uint16_t* k_cache,
+                                        const uint16_t* v_cache, const int32_t* block_table,
+                                        const int32_t* context_lens, float* out,
+                                        int32_t* selected, float* lse, void* workspace,
+                                        size_t workspace_bytes, int dense,
+                                        hipEvent_t* stage_events, hipStream_t stream);
+
+/* Byte offsets of the intermediate arrays inside the decode workspace, so
+ * tests can check each stage.  Layouts (bh = b * Hkv + h):
+ *   lut     float [B*Hkv][16][256][G]  scale*log2(e) * q_g^(m) . B_m[j]
+ *   qc      float [B*Hkv][L][G]        scale*log2(e) * q_g . C_c
+ *   keys    uint32 [B*Hkv][max_context] order-preserving bits of each index
+ *           entry's key (cluster order; 0 for non-candidates)
+ *   bins    float [B*Hkv][L][G][2]     per cluster: max and sum of exp2 of
+ *           the candidates' base-2 logits relative to that max
+ *   rows    int32 [B*Hkv][max_context] exact rows: sink, selected, recent/tail
+ *   n_rows  int32 [B*Hkv]
+ *   partials float [B][Hq][n_parts][132]: (m in base 2, l, pad, pad, acc[128]) */
+typedef struct pqhsa_ws_layout {
+  size_t lut, qc, keys, bins, rows, n_rows, partials;
+  int32_t n_exact_splits, n_bg_splits, n_parts;
+} pqhsa_ws_layout;
+pqhsa_status pqhsa_workspace_layout(const pqhsa_shape* shape, int dense, pqhsa_ws_layout* out);
+
+/* Byte offsets of the index arrays inside index_buf (bh = b * Hkv + h):
+ *   centroids float [B*Hkv][L][128], codebooks float [B*Hkv][16][256][8],
+ *   list_off int32 [B*Hkv][L+1] (entries of cluster c are [list_off[c], list_off[c+1])),
+ *   codes uint8 [B*Hkv][max_context][16], pos int32 [B*Hkv][max_context],
+ *   means float [B*Hkv][L][128], n_indexed int32 [B]. */
+typedef struct pqhsa_index_layout {
+  size_t centroids, codebooks, list_off, codes, pos, means, n_indexed, dropped;
+} pqhsa_index_layout;
+pqhsa_status pqhsa_index_layout_of(const pqhsa_shape* shape, pqhsa_index_layout* out);
+
+/* Static description of a status code. */
+const char* pqhsa_status_string(pqhsa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PQHSA_H */

@@ -1,0 +1,92 @@
+"""PQ-HSA decode attention for AMD Instinct MI355X (gfx950).
+
+Python face of libpqhsa (include/pqhsa.h).  The functions in `_lib` mirror
+the C entry points one to one; `PQHSADecoder` owns the index buffer and the
+workspaces that those entry points need.  torch supplies device memory and
+streams; all computation runs in the HIP kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    NUM_STAGES,
+    STAGE_NAMES,
+    HipEvent,
+    PQHSAError,
+    Shape,
+    decode_step,
+    decode_step_profiled,
+    dense_decode_step,
+    index_bytes,
+    index_dropped,
+    index_layout,
+    load,
+    make_shape,
+    max_selected,
+    status_string,
+    upload_index,
+    upload_workspace_bytes,
+    workspace_bytes,
+    workspace_layout,
+)
+
+
+class PQHSADecoder:
+    """Owns one index buffer and the step workspaces for a fixed shape.
+
+    upload() builds the index once; step() runs one PQ-HSA decode step and
+    dense() the dense split-K baseline, both on the current torch stream.
+    """
+
+    def __init__(self, shape: Shape, device="cuda"):
+        load()
+        self.shape = shape
+        self.device = torch.device(device)
+        nb = index_bytes(shape)
+        if nb == 0:
+            raise PQHSAError("pqhsa_index_bytes", 1)
+        self.index = torch.empty(nb, dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(workspace_bytes(shape, False), dtype=torch.uint8,
+                                     device=self.device)
+        self._dense_ws = None
+        self.max_selected = max_selected(shape)
+
+    def upload(self, centroids, codebooks, list_ids, codes, n_indexed, v_cache, block_table,
+               stream=None):
+        ws = torch.empty(max(upload_workspace_bytes(self.shape), 1), dtype=torch.uint8,
+                         device=self.device)
+        upload_index(self.shape, centroids, codebooks, list_ids, codes, n_indexed, v_cache,
+                     block_table, self.index, ws, stream)
+        self._upload_ws = ws          # keep alive until the stream has used it
+
+    def step(self, q, k_cache, v_cache, block_table, context_lens, out=None, selected=False,
+             lse=False, stream=None):
+        s = self.shape
+        if out is None:
+            out = torch.empty(s.batch, s.num_q_heads, 128, dtype=torch.float32, device=self.device)
+        # -1 marks unused slots; with a zero budget the library writes none
+        sel = (torch.full((s.batch, s.num_kv_heads, max(self.max_selected, 1)), -1,
+                          dtype=torch.int32, device=self.device) if selected else None)
+        ls = torch.empty(s.batch, s.num_q_heads, dtype=torch.float32, device=self.device) if lse else None
+        decode_step(s, self.index, q, k_cache, v_cache, block_table, context_lens, out,
+                    self.workspace, selected=sel, lse=ls, stream=stream)
+        return out, sel, ls
+
+    def dense_workspace(self):
+        if self._dense_ws is None:
+            self._dense_ws = torch.empty(workspace_bytes(self.shape, True), dtype=torch.uint8,
+                                         device=self.device)
+        return self._dense_ws
+
+    def dense(self, q, k_cache, v_cache, block_table, context_lens, out=None, lse=False,
+              stream=None):
+        s = self.shape
+        if out is None:
+            out = torch.empty(s.batch, s.num_q_heads, 128, dtype=torch.float32, device=self.device)
+        ls = torch.empty(s.batch, s.num_q_heads, dtype=torch.float32, device=self.device) if lse else None
+        dense_decode_step(s, q, k_cache, v_cache, block_table, context_lens, out,
+                          self.dense_workspace(), lse=ls, stream=stream)
+        return out, ls

@@ -1,0 +1,380 @@
+// C ABI of libpqhsa: argument validation, buffer layouts and launch order.
+// The operations themselves are documented in include/pqhsa.h.
+#include <math.h>
+#include <string.h>
+
+#include "pqhsa_internal.hpp"
+
+using namespace pqhsa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxContextLimit = 1 << 26;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+pqhsa_status validate(const pqhsa_shape* s, bool dense) {
+  if (!s) return PQHSA_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1) return PQHSA_ERR_INVALID_ARG;
+  if (s->num_q_heads % s->num_kv_heads != 0) return PQHSA_ERR_INVALID_ARG;
+  if (s->head_dim < 1 || s->page_size < 1) return PQHSA_ERR_INVALID_ARG;
+  if (s->num_pages < 1 || s->max_pages_per_seq < 1 || s->max_context < 1)
+    return PQHSA_ERR_INVALID_ARG;
+  if ((long long)s->max_context > (long long)s->max_pages_per_seq * s->page_size)
+    return PQHSA_ERR_INVALID_ARG;
+  if (s->max_context > kMaxContextLimit) return PQHSA_ERR_UNSUPPORTED;
+  if (!(s->scale > 0.0f) || !isfinite(s->scale)) return PQHSA_ERR_INVALID_ARG;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PQHSA_ERR_UNSUPPORTED;
+  if (s->head_dim != kD || s->page_size != kPage) return PQHSA_ERR_UNSUPPORTED;
+  // the K/V cache offsets are formed in 64-bit; page indices in 32-bit
+  if ((long long)s->num_pages * kPage > 0x7fffffffLL) return PQHSA_ERR_UNSUPPORTED;
+  if (dense) return PQHSA_OK;
+  if (s->num_lists < 1 || s->pq_m < 1 || s->pq_ksub < 1) return PQHSA_ERR_INVALID_ARG;
+  if (s->n_sink < 0 || s->n_recent < 0) return PQHSA_ERR_INVALID_ARG;
+  if (s->budget_bp < 0 || s->budget_bp > 10000) return PQHSA_ERR_INVALID_ARG;
+  if (s->num_lists > kMaxLists) return PQHSA_ERR_UNSUPPORTED;
+  if (s->pq_m != kM || s->pq_ksub != kKsub) return PQHSA_ERR_UNSUPPORTED;
+  return PQHSA_OK;
+}
+
+int max_selected(const pqhsa_shape* s) {
+  const long long k = ((long long)s->max_context * s->budget_bp + 9999) / 10000;
+  return (int)(k < s->max_context ? k : s->max_context);
+}
+
+Dims make_dims(const pqhsa_shape* s, bool dense) {
+  Dims d;
+  memset(&d, 0, sizeof(d));
+  d.B = s->batch;
+  d.Hq = s->num_q_heads;
+  d.Hkv = s->num_kv_heads;
+  d.G = d.Hq / d.Hkv;
+  d.L = dense ? 1 : s->num_lists;
+  d.num_pages = s->num_pages;
+  d.max_pages = s->max_pages_per_seq;
+  d.cap = s->max_context;
+  d.n_sink = dense ? 0 : s->n_sink;
+  d.n_recent = dense ? 0 : s->n_recent;
+  d.budget_bp = dense ? 0 : s->budget_bp;
+  d.scale_log2 = (float)((double)s->scale * 1.4426950408889634);
+  d.nwords = ceil_div(d.cap, 32);
+  d.scan_blocks = ceil_div(d.L, kScanListsPerBlock);
+  d.collect_slices = ceil_div(d.cap, kCollectEntries);
+  d.upload_chunks = ceil_div(d.cap, kUploadChunk);
+  if (dense) {
+    d.n_exact_splits = ceil_div(d.cap, kDenseRowsPerSplit);
+    d.n_bg_splits = 0;
+  } else {
+    const long long rows_est = (long long)s->n_sink + s->n_recent + max_selected(s) + 512;
+    int n = ceil_div(rows_est, kExactRowsPerSplit);
+    d.n_exact_splits = n < 1 ? 1 : (n > 4096 ? 4096 : n);
+    d.n_bg_splits = ceil_div(d.L, kBgListsPerBlock);
+  }
+  d.n_parts = d.n_exact_splits + d.n_bg_splits;
+  return d;
+}
+
+struct IndexLayout {
+  size_t centroids, codebooks, list_off, codes, pos, means, n_indexed, dropped, total;
+};
+
+IndexLayout index_layout(const Dims& d) {
+  IndexLayout l;
+  const size_t BH = (size_t)d.B * d.Hkv;
+  size_t o = 0;
+  l.centroids = o; o = align_up(o + BH * d.L * kD * sizeof(float));
+  l.codebooks = o; o = align_up(o + BH * kM * kKsub * kDsub * sizeof(float));
+  l.list_off = o;  o = align_up(o + BH * (d.L + 1) * sizeof(int32_t));
+  l.codes = o;     o = align_up(o + BH * d.cap * kM);
+  l.pos = o;       o = align_up(o + BH * d.cap * sizeof(int32_t));
+  l.means = o;     o = align_up(o + BH * d.L * kD * sizeof(float));
+  l.n_indexed = o; o = align_up(o + (size_t)d.B * sizeof(int32_t));
+  l.dropped = o;   o = align_up(o + sizeof(unsigned long long));
+  l.total = o;
+  return l;
+}
+
+struct WsLayout {
+  size_t lut, qc, keys, bins, hist, cand_count, cand, sel_p, sel_e, rows, n_rows, partials, total;
+};
+
+WsLayout ws_layout(const Dims& d, bool dense) {
+  WsLayout l;
+  memset(&l, 0, sizeof(l));
+  const size_t BH = (size_t)d.B * d.Hkv;
+  size_t o = 0;
+  if (!dense) {
+    l.lut = o;        o = align_up(o + BH * kM * kKsub * d.G * sizeof(float));
+    l.qc = o;         o = align_up(o + BH * d.L * d.G * sizeof(float));
+    l.keys = o;       o = align_up(o + BH * d.cap * sizeof(uint32_t));
+    l.bins = o;       o = align_up(o + BH * d.L * d.G * 2 * sizeof(float));
+    l.hist = o;       o = align_up(o + BH * kHistBins * sizeof(uint32_t));
+    l.cand_count = o; o = align_up(o + BH * sizeof(uint32_t));
+    l.cand = o;       o = align_up(o + BH * d.cap * sizeof(uint4));
+    l.sel_p = o;      o = align_up(o + BH * d.nwords * sizeof(uint32_t));
+    l.sel_e = o;      o = align_up(o + BH * d.nwords * sizeof(uint32_t));
+    l.rows = o;       o = align_up(o + BH * d.cap * sizeof(int32_t));
+    l.n_rows = o;     o = align_up(o + BH * sizeof(int32_t));
+  }
+  l.partials = o;     o = align_up(o + (size_t)d.B * d.Hq * d.n_parts * kPart * sizeof(float));
+  l.total = o;
+  return l;
+}
+
+size_t upload_ws_bytes(const Dims& d) {
+  return align_up((size_t)d.B * d.Hkv * d.upload_chunks * d.L * sizeof(int32_t));
+}
+
+IndexPtrs index_ptrs(const Dims& d, void* buf) {
+  const IndexLayout l = index_layout(d);
+  char* p = static_cast<char*>(buf);
+  IndexPtrs ix;
+  ix.centroids = reinterpret_cast<float*>(p + l.centroids);
+  ix.codebooks = reinterpret_cast<float*>(p + l.codebooks);
+  ix.list_off = reinterpret_cast<int32_t*>(p + l.list_off);
+  ix.codes = reinterpret_cast<uint8_t*>(p + l.codes);
+  ix.pos = reinterpret_cast<int32_t*>(p + l.pos);
+  ix.means = reinterpret_cast<float*>(p + l.means);
+  ix.n_indexed = reinterpret_cast<int32_t*>(p + l.n_indexed);
+  ix.dropped = reinterpret_cast<unsigned long long*>(p + l.dropped);
+  return ix;
+}
+
+WsPtrs ws_ptrs(const Dims& d, bool dense, void* buf) {
+  const WsLayout l = ws_layout(d, dense);
+  char* p = static_cast<char*>(buf);
+  WsPtrs w;
+  memset(&w, 0, sizeof(w));
+  if (!dense) {
+    w.lut = reinterpret_cast<float*>(p + l.lut);
+    w.qc = reinterpret_cast<float*>(p + l.qc);
+    w.keys = reinterpret_cast<uint32_t*>(p + l.keys);
+    w.bins = reinterpret_cast<float*>(p + l.bins);
+    w.hist = reinterpret_cast<uint32_t*>(p + l.hist);
+    w.cand_count = reinterpret_cast<uint32_t*>(p + l.cand_count);
+    w.cand = reinterpret_cast<uint4*>(p + l.cand);
+    w.sel_p = reinterpret_cast<uint32_t*>(p + l.sel_p);
+    w.sel_e = reinterpret_cast<uint32_t*>(p + l.sel_e);
+    w.rows = reinterpret_cast<int32_t*>(p + l.rows);
+    w.n_rows = reinterpret_cast<int32_t*>(p + l.n_rows);
+  }
+  w.partials = reinterpret_cast<float*>(p + l.partials);
+  return w;
+}
+
+inline pqhsa_status hip_status(hipError_t e) { return e == hipSuccess ? PQHSA_OK : PQHSA_ERR_HIP; }
+
+pqhsa_status record(hipEvent_t* evs, int i, hipStream_t st) {
+  if (!evs) return PQHSA_OK;
+  return hip_status(hipEventRecord(evs[i], st));
+}
+
+#define PQHSA_TRY(expr)                         \
+  do {                                          \
+    pqhsa_status s_ = (expr);                   \
+    if (s_ != PQHSA_OK) return s_;              \
+  } while (0)
+
+pqhsa_status run_dense(const pqhsa_shape* shape, const uint16_t* q, const uint16_t* k_cache,
+                       const uint16_t* v_cache, const int32_t* block_table,
+                       const int32_t* context_lens, float* out, float* lse, void* workspace,
+                       size_t ws_bytes, hipEvent_t* evs, hipStream_t stream) {
+  PQHSA_TRY(validate(shape, true));
+  if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out || !workspace)
+    return PQHSA_ERR_INVALID_ARG;
+  const Dims d = make_dims(shape, true);
+  if (ws_bytes < ws_layout(d, true).total) return PQHSA_ERR_BUFFER_TOO_SMALL;
+  StepArgs a;
+  memset(&a, 0, sizeof(a));
+  a.d = d;
+  a.ws = ws_ptrs(d, true, workspace);
+  a.q = q; a.kc = k_cache; a.vc = v_cache; a.table = block_table; a.ctx = context_lens;
+  a.out = out; a.lse = lse;
+  PQHSA_TRY(record(evs, 0, stream));
+  PQHSA_TRY(hip_status(launch_exact_and_background(a, true, stream)));
+  PQHSA_TRY(record(evs, 1, stream));
+  PQHSA_TRY(hip_status(launch_merge(a, stream)));
+  PQHSA_TRY(record(evs, 2, stream));
+  return PQHSA_OK;
+}
+
+pqhsa_status run_step(const pqhsa_shape* shape, const void* index_buf, const uint16_t* q,
+                      const uint16_t* k_cache, const uint16_t* v_cache,
+                      const int32_t* block_table, const int32_t* context_lens, float* out,
+                      int32_t* selected, float* lse, void* workspace, size_t ws_bytes,
+                      hipEvent_t* evs, hipStream_t stream) {
+  PQHSA_TRY(validate(shape, false));
+  if (!index_buf || !q || !k_cache || !v_cache || !block_table || !context_lens || !out ||
+      !workspace)
+    return PQHSA_ERR_INVALID_ARG;
+  const Dims d = make_dims(shape, false);
+  if (ws_bytes < ws_layout(d, false).total) return PQHSA_ERR_BUFFER_TOO_SMALL;
+  StepArgs a;
+  memset(&a, 0, sizeof(a));
+  a.d = d;
+  a.ix = index_ptrs(d, const_cast<void*>(index_buf));
+  a.ws = ws_ptrs(d, false, workspace);
+  a.q = q; a.kc = k_cache; a.vc = v_cache; a.table = block_table; a.ctx = context_lens;
+  a.out = out; a.selected = selected; a.max_sel = max_selected(shape); a.lse = lse;
+  PQHSA_TRY(record(evs, PQHSA_STAGE_TABLES, stream));
+  PQHSA_TRY(hip_status(launch_tables(a, stream)));
+  PQHSA_TRY(record(evs, PQHSA_STAGE_SCAN, stream));
+  PQHSA_TRY(hip_status(launch_scan(a, stream)));
+  PQHSA_TRY(record(evs, PQHSA_STAGE_COLLECT, stream));
+  PQHSA_TRY(hip_status(launch_collect(a, stream)));
+  PQHSA_TRY(record(evs, PQHSA_STAGE_SELECT, stream));
+  PQHSA_TRY(hip_status(launch_select(a, stream)));
+  PQHSA_TRY(record(evs, PQHSA_STAGE_EXACT, stream));
+  PQHSA_TRY(hip_status(launch_exact_and_background(a, false, stream)));
+  PQHSA_TRY(record(evs, PQHSA_STAGE_MERGE, stream));
+  PQHSA_TRY(hip_status(launch_merge(a, stream)));
+  PQHSA_TRY(record(evs, PQHSA_NUM_STAGES, stream));
+  return PQHSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pqhsa_index_bytes(const pqhsa_shape* shape) {
+  if (validate(shape, false) != PQHSA_OK) return 0;
+  return index_layout(make_dims(shape, false)).total;
+}
+
+size_t pqhsa_upload_workspace_bytes(const pqhsa_shape* shape) {
+  if (validate(shape, false) != PQHSA_OK) return 0;
+  return upload_ws_bytes(make_dims(shape, false));
+}
+
+size_t pqhsa_workspace_bytes(const pqhsa_shape* shape, int dense) {
+  if (validate(shape, dense != 0) != PQHSA_OK) return 0;
+  return ws_layout(make_dims(shape, dense != 0), dense != 0).total;
+}
+
+int32_t pqhsa_max_selected(const pqhsa_shape* shape) {
+  if (validate(shape, false) != PQHSA_OK) return 0;
+  return max_selected(shape);
+}
+
+pqhsa_status pqhsa_upload_index(const pqhsa_shape* shape, const float* centroids,
+                                const float* codebooks, const int32_t* list_ids,
+                                const uint8_t* codes, const int32_t* n_indexed,
+                                const uint16_t* v_cache, const int32_t* block_table,
+                                void* index_buf, size_t index_bytes, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  PQHSA_TRY(validate(shape, false));
+  if (!centroids || !codebooks || !list_ids || !codes || !n_indexed || !v_cache ||
+      !block_table || !index_buf || !workspace)
+    return PQHSA_ERR_INVALID_ARG;
+  const Dims d = make_dims(shape, false);
+  if (index_bytes < index_layout(d).total) return PQHSA_ERR_BUFFER_TOO_SMALL;
+  if (workspace_bytes < upload_ws_bytes(d)) return PQHSA_ERR_BUFFER_TOO_SMALL;
+  UploadArgs a;
+  memset(&a, 0, sizeof(a));
+  a.d = d;
+  a.ix = index_ptrs(d, index_buf);
+  a.list_ids = list_ids;
+  a.codes = codes;
+  a.n_indexed = n_indexed;
+  a.vc = v_cache;
+  a.table = block_table;
+  a.chunk_counts = static_cast<int32_t*>(workspace);
+  const size_t BH = (size_t)d.B * d.Hkv;
+  PQHSA_TRY(hip_status(hipMemcpyAsync(a.ix.centroids, centroids, BH * d.L * kD * sizeof(float),
+                                      hipMemcpyDeviceToDevice, stream)));
+  PQHSA_TRY(hip_status(hipMemcpyAsync(a.ix.codebooks, codebooks,
+                                      BH * kM * kKsub * kDsub * sizeof(float),
+                                      hipMemcpyDeviceToDevice, stream)));
+  PQHSA_TRY(hip_status(hipMemcpyAsync(a.ix.n_indexed, n_indexed, d.B * sizeof(int32_t),
+                                      hipMemcpyDeviceToDevice, stream)));
+  PQHSA_TRY(hip_status(hipMemsetAsync(a.ix.dropped, 0, sizeof(unsigned long long), stream)));
+  return hip_status(launch_upload(a, stream));
+}
+
+pqhsa_status pqhsa_index_dropped(const pqhsa_shape* shape, const void* index_buf,
+                                 int64_t* dropped, hipStream_t stream) {
+  PQHSA_TRY(validate(shape, false));
+  if (!index_buf || !dropped) return PQHSA_ERR_INVALID_ARG;
+  const Dims d = make_dims(shape, false);
+  const IndexLayout l = index_layout(d);
+  unsigned long long v = 0;
+  PQHSA_TRY(hip_status(hipMemcpyAsync(&v, static_cast<const char*>(index_buf) + l.dropped,
+                                      sizeof(v), hipMemcpyDeviceToHost, stream)));
+  PQHSA_TRY(hip_status(hipStreamSynchronize(stream)));
+  *dropped = (int64_t)v;
+  return PQHSA_OK;
+}
+
+pqhsa_status pqhsa_decode_step(const pqhsa_shape* shape, const void* index_buf,
+                               const uint16_t* q, const uint16_t* k_cache,
+                               const uint16_t* v_cache, const int32_t* block_table,
+                               const int32_t* context_lens, float* out, int32_t* selected,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  return run_step(shape, index_buf, q, k_cache, v_cache, block_table, context_lens, out,
+                  selected, lse, workspace, workspace_bytes, nullptr, stream);
+}
+
+pqhsa_status pqhsa_dense_decode_step(const pqhsa_shape* shape, const uint16_t* q,
+                                     const uint16_t* k_cache, const uint16_t* v_cache,
+                                     const int32_t* block_table, const int32_t* context_lens,
+                                     float* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  return run_dense(shape, q, k_cache, v_cache, block_table, context_lens, out, lse, workspace,
+                   workspace_bytes, nullptr, stream);
+}
+
+pqhsa_status pqhsa_decode_step_profiled(const pqhsa_shape* shape, const void* index_buf,
+                                        const uint16_t* q, const uint16_t* k_cache,
+                                        const uint16_t* v_cache, const int32_t* block_table,
+                                        const int32_t* context_lens, float* out,
+                                        int32_t* selected, float* lse, void* workspace,
+                                        size_t workspace_bytes, int dense,
+                                        hipEvent_t* stage_events, hipStream_t stream) {
+  if (!stage_events) return PQHSA_ERR_INVALID_ARG;
+  if (dense)
+    return run_dense(shape, q, k_cache, v_cache, block_table, context_lens, out, lse, workspace,
+                     workspace_bytes, stage_events, stream);
+  return run_step(shape, index_buf, q, k_cache, v_cache, block_table, context_lens, out,
+                  selected, lse, workspace, workspace_bytes, stage_events, stream);
+}
+
+pqhsa_status pqhsa_workspace_layout(const pqhsa_shape* shape, int dense, pqhsa_ws_layout* out) {
+  PQHSA_TRY(validate(shape, dense != 0));
+  if (!out) return PQHSA_ERR_INVALID_ARG;
+  const Dims d = make_dims(shape, dense != 0);
+  const WsLayout l = ws_layout(d, dense != 0);
+  out->lut = l.lut; out->qc = l.qc; out->keys = l.keys; out->bins = l.bins;
+  out->rows = l.rows; out->n_rows = l.n_rows; out->partials = l.partials;
+  out->n_exact_splits = d.n_exact_splits;
+  out->n_bg_splits = d.n_bg_splits;
+  out->n_parts = d.n_parts;
+  return PQHSA_OK;
+}
+
+pqhsa_status pqhsa_index_layout_of(const pqhsa_shape* shape, pqhsa_index_layout* out) {
+  PQHSA_TRY(validate(shape, false));
+  if (!out) return PQHSA_ERR_INVALID_ARG;
+  const IndexLayout l = index_layout(make_dims(shape, false));
+  out->centroids = l.centroids; out->codebooks = l.codebooks; out->list_off = l.list_off;
+  out->codes = l.codes; out->pos = l.pos; out->means = l.means; out->n_indexed = l.n_indexed;
+  out->dropped = l.dropped;
+  return PQHSA_OK;
+}
+
+const char* pqhsa_status_string(pqhsa_status status) {
+  switch (status) {
+    case PQHSA_OK: return "ok";
+    case PQHSA_ERR_INVALID_ARG: return "invalid argument";
+    case PQHSA_ERR_UNSUPPORTED: return "unsupported shape";
+    case PQHSA_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case PQHSA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,200 @@
+// Internal declarations of libpqhsa: argument blocks, device helpers and the
+// kernel launchers shared by the translation units.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pqhsa.h"
+
+namespace pqhsa {
+
+constexpr int kD = 128;          // head_dim
+constexpr int kPage = 16;        // tokens per cache page
+constexpr int kM = 16;           // PQ subspaces
+constexpr int kKsub = 256;       // codewords per subspace
+constexpr int kDsub = 8;         // dims per subspace
+constexpr int kHistBits = 12;    // top bits of a key used by the first selection pass
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kPart = 132;       // floats per partial: m (base 2), l, pad, pad, acc[128]
+constexpr int kMaxLists = 16384;
+constexpr int kScanThreads = 1024;
+constexpr int kScanListsPerBlock = 16;
+constexpr int kCollectEntries = 4096;   // index entries per collect block
+constexpr int kExactRowsPerSplit = 64;  // target rows per split-K block (index-list mode)
+constexpr int kDenseRowsPerSplit = 512; // rows per split-K block (dense mode)
+constexpr int kBgListsPerBlock = 64;
+constexpr int kUploadChunk = 4096;      // tokens per counting-sort chunk
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Shape-derived sizes, passed to every kernel by value.
+struct Dims {
+  int B, Hq, Hkv, G, L, num_pages, max_pages, cap;
+  int n_sink, n_recent, budget_bp;
+  float scale_log2;           // scale * log2(e): logits are kept in base 2
+  int nwords;                 // ceil(cap / 32): words of a per-head bitmap
+  int scan_blocks;            // scan blocks per (b, h)
+  int collect_slices;         // collect blocks per (b, h)
+  int n_exact_splits;         // split-K blocks per (b, h)
+  int n_bg_splits;            // background blocks per (b, h)
+  int n_parts;                // partials per (b, q head)
+  int upload_chunks;          // counting-sort chunks per (b, h)
+};
+
+struct IndexPtrs {
+  float* centroids;    // [BH][L][128]
+  float* codebooks;    // [BH][16][256][8]
+  int32_t* list_off;   // [BH][L+1]
+  uint8_t* codes;      // [BH][cap][16] cluster order
+  int32_t* pos;        // [BH][cap]     token position of each entry
+  float* means;        // [BH][L][128]
+  int32_t* n_indexed;  // [B]
+  unsigned long long* dropped;  // [1]
+};
+
+struct WsPtrs {
+  float* lut;          // [BH][16][256][G]
+  float* qc;           // [BH][L][G]
+  uint32_t* keys;      // [BH][cap]
+  float* bins;         // [BH][L][G][2]
+  uint32_t* hist;      // [BH][4096]
+  uint32_t* cand_count;// [BH]
+  uint4* cand;         // [BH][cap]  (key, pos, entry, 0)
+  uint32_t* sel_p;     // [BH][nwords] bitmap over positions
+  uint32_t* sel_e;     // [BH][nwords] bitmap over index entries
+  int32_t* rows;       // [BH][cap]
+  int32_t* n_rows;     // [BH]
+  float* partials;     // [B][Hq][n_parts][132]
+};
+
+struct StepArgs {
+  Dims d;
+  IndexPtrs ix;
+  WsPtrs ws;
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int32_t* table;
+  const int32_t* ctx;
+  float* out;
+  int32_t* selected;
+  int32_t max_sel;
+  float* lse;
+};
+
+struct UploadArgs {
+  Dims d;
+  IndexPtrs ix;
+  const int32_t* list_ids;   // [BH][cap]
+  const uint8_t* codes;      // [BH][cap][16]
+  const int32_t* n_indexed;  // [B]
+  const uint16_t* vc;
+  const int32_t* table;
+  int32_t* chunk_counts;     // [BH][chunks][L]
+};
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Order-preserving map float -> uint32 (larger float, larger integer).  Every
+// non-NaN float maps above 0, which is reserved for "not a candidate".
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the total.
+// quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror, row_mirror.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  x += dpp_f<0x140>(x);
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Per-sequence quantities of the forced/candidate split.
+struct SeqInfo {
+  int T;          // context length (clamped to [0, cap])
+  int ns;         // sink rows actually present, min(n_sink, T)
+  int cand_beg;   // candidates are positions [cand_beg, cand_end)
+  int cand_end;
+  int n_cand;
+  int k;          // budget, min(ceil(T*bp/10000), n_cand)
+  int recent_beg; // exact rows [recent_beg, T) after the selected ones
+};
+
+__device__ __forceinline__ SeqInfo seq_info(const Dims& d, const int32_t* ctx,
+                                            const int32_t* n_indexed, int b) {
+  SeqInfo s;
+  int T = min(max(ctx[b], 0), d.cap);
+  int Ti = min(max(n_indexed[b], 0), T);
+  int R = max(d.n_recent, T - Ti);
+  s.T = T;
+  s.ns = min(d.n_sink, T);
+  s.cand_beg = d.n_sink;
+  s.cand_end = T - R;
+  s.n_cand = max(s.cand_end - s.cand_beg, 0);
+  long long kk = ((long long)T * d.budget_bp + 9999) / 10000;
+  s.k = (int)min((long long)s.n_cand, kk);
+  s.recent_beg = max(T - R, s.ns);
+  return s;
+}
+
+// Approximate base-2 logits of one index entry for the G query heads of its
+// KV head: qc_g + sum_m lut[m][code_m][g], summed in subspace order.  The scan
+// and the background kernel both call this, so an entry's value is
+// bit-identical in both.
+template <int G>
+__device__ __forceinline__ void entry_logits(const float* __restrict__ lut, const float* qc,
+                                             uint4 cw, float* s) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) s[g] = qc[g];
+  const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    const uint32_t code = (w[m >> 2] >> ((m & 3) * 8)) & 0xffu;
+    const float* e = lut + (m * kKsub + code) * G;
+    if constexpr (G == 8) {
+      float4 a = *reinterpret_cast<const float4*>(e);
+      float4 c = *reinterpret_cast<const float4*>(e + 4);
+      s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+      s[4] += c.x; s[5] += c.y; s[6] += c.z; s[7] += c.w;
+    } else if constexpr (G == 4) {
+      float4 a = *reinterpret_cast<const float4*>(e);
+      s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+    } else if constexpr (G == 2) {
+      float2 a = *reinterpret_cast<const float2*>(e);
+      s[0] += a.x; s[1] += a.y;
+    } else {
+      s[0] += e[0];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_upload(const UploadArgs& a, hipStream_t st);
+hipError_t launch_tables(const StepArgs& a, hipStream_t st);
+hipError_t launch_scan(const StepArgs& a, hipStream_t st);
+hipError_t launch_collect(const StepArgs& a, hipStream_t st);
+hipError_t launch_select(const StepArgs& a, hipStream_t st);
+hipError_t launch_exact_and_background(const StepArgs& a, bool dense, hipStream_t st);
+hipError_t launch_merge(const StepArgs& a, hipStream_t st);
+
+}  // namespace pqhsa

@@ -1,0 +1,186 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64 oracle."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import ivf_pq_sparse_amd as pq
+    pq.load()          # raises if the HIP library is not built: no fallback
+
+
+from gpu_helpers import (check_output, log, oracle_with_details, parity,  # noqa: E402
+                         run_gpu)
+from pqhsa_synth import make_step_inputs  # noqa: E402
+
+
+# ------------------------------------------------------------------ dense baseline
+@pytest.mark.parametrize("T,G,Hkv", [(8192, 4, 1), (1000, 4, 2), (37, 8, 1), (5000, 1, 3),
+                                     (2049, 2, 2)])
+def test_dense_matches_oracle(T, G, Hkv):
+    import oracle
+    inp = make_step_inputs(0, context_lens=[T], num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                           num_lists=8, workload_id=500 + T)
+    log(f"[dense] T={T} G={G} Hkv={Hkv}")
+    g = run_gpu(inp, dense=True)
+    ref = oracle.dense_step(inp)
+    check_output(g["O"], ref, f"dense T={T}")
+
+
+def test_dense_variable_lengths_and_spare_pages():
+    import oracle
+    inp = make_step_inputs(1, context_lens=[3000, 17, 1024, 2500], batch=4, num_q_heads=8,
+                           num_kv_heads=2, num_lists=16, workload_id=77)
+    log("[dense] ragged batch")
+    g = run_gpu(inp, dense=True, spare_pages=9, page_seed=3, max_context=3100)
+    check_output(g["O"], oracle.dense_step(inp), "dense ragged")
+
+
+# ------------------------------------------------------------------ PQ-HSA step
+def test_tiny_workload_parity():
+    parity(make_step_inputs(0), what="workload 0 (8K, 4q/1kv, L64)")
+
+
+def test_llama_32k_parity():
+    parity(make_step_inputs(1), what="workload 1 (32K, 32q/8kv, L256)")
+
+
+def test_full_budget_is_dense_on_gpu():
+    import oracle
+    inp = make_step_inputs(1, context_lens=[4100], budget_bp=10000, num_lists=32, workload_id=9)
+    log("[pqhsa] budget 100 %")
+    g = run_gpu(inp)
+    check_output(g["O"], oracle.dense_step(inp), "budget 100% vs dense")
+    parity(inp, what="budget 100 %")
+
+
+def test_budget_zero():
+    inp = make_step_inputs(0, context_lens=[3000], budget_bp=0, num_lists=16, workload_id=10)
+    g, _, _ = parity(inp, what="budget 0")
+    assert all(v.size == 0 for v in g["selected"].values())
+
+
+def test_one_token_clusters_zero_noise_equal_dense():
+    import oracle
+    T = 2048
+    inp = make_step_inputs(0, context_lens=[T], dyadic=True, num_lists=T, one_token_per_list=True,
+                           budget_bp=100, workload_id=11)
+    log("[pqhsa] one token per cluster, zero noise")
+    g = run_gpu(inp)
+    check_output(g["O"], oracle.dense_step(inp), "one-token clusters vs dense")
+
+
+def test_exact_ties_pick_lower_positions():
+    # copy one candidate's (list, codes) over many others: their keys tie exactly
+    inp = make_step_inputs(0, context_lens=[2000], num_lists=16, budget_bp=100, workload_id=12,
+                           noise=0.0)
+    ref = oracle_with_details(inp)
+    kap, cand = ref["kappa"][(0, 0)], ref["candidates"][(0, 0)]
+    src = int(cand[np.argmax(kap[cand])])
+    dups = np.arange(100, 1900, 37)
+    dups = dups[dups != src]
+    inp.list_ids[0, 0, dups] = inp.list_ids[0, 0, src]
+    inp.codes[0, 0, dups] = inp.codes[0, 0, src]
+    g, ref, _ = parity(inp, what="exact ties")
+    k = ref["k"][(0, 0)]
+    tied = np.sort(np.concatenate([dups, [src]]))
+    assert k < tied.size
+    assert g["selected"][(0, 0)].tolist() == tied[:k].tolist()
+
+
+def test_recent_longer_than_tail_and_ragged_batch():
+    inp = make_step_inputs(1, context_lens=[5000, 3333, 777, 4096], batch=4, num_q_heads=8,
+                           num_kv_heads=2, num_lists=64, n_tail=40, n_recent=200, n_sink=7,
+                           budget_bp=250, workload_id=13)
+    parity(inp, what="recent > tail, ragged batch", max_context=5003, page_seed=5)
+
+
+def test_everything_forced_and_nothing_indexed():
+    # sink + recent cover the context; and a sequence with no indexed token
+    inp = make_step_inputs(1, context_lens=[300, 500], batch=2, num_q_heads=4, num_kv_heads=1,
+                           num_lists=8, n_sink=100, n_recent=250, n_tail=0, budget_bp=500,
+                           workload_id=14)
+    parity(inp, what="all forced")
+    inp2 = make_step_inputs(1, context_lens=[700], num_q_heads=4, num_kv_heads=1, num_lists=8,
+                            n_tail=700, budget_bp=100, workload_id=15)
+    g, _, _ = parity(inp2, what="empty index")
+    assert g["selected"][(0, 0)].size == 0
+
+
+def test_gqa_group_sizes():
+    for G, Hkv in [(1, 4), (2, 2), (8, 1)]:
+        inp = make_step_inputs(1, context_lens=[6000], num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                               num_lists=48, budget_bp=150, workload_id=20 + G)
+        parity(inp, what=f"G={G}")
+
+
+def test_index_means_match_oracle():
+    import ivf_pq_sparse_amd as pq
+    from oracle import pqhsa_oracle as orc
+    inp = make_step_inputs(1, context_lens=[3000, 2000], batch=2, num_q_heads=8, num_kv_heads=2,
+                           num_lists=40, workload_id=30)
+    g = run_gpu(inp)
+    shape, dec = g["shape"], g["dec"]
+    lay = pq.index_layout(shape)
+    L = shape.num_lists
+    buf = dec.index
+    means = buf[lay.means:lay.means + 2 * 2 * L * 128 * 4].view(torch.float32).cpu().numpy()
+    means = means.reshape(2, 2, L, 128)
+    off = buf[lay.list_off:lay.list_off + 2 * 2 * (L + 1) * 4].view(torch.int32).cpu().numpy()
+    off = off.reshape(2, 2, L + 1)
+    for b in range(2):
+        Ti = int(inp.n_indexed[b])
+        for h in range(2):
+            mu = orc.cluster_means(orc.bf16_to_f64(inp.v_bits[b, h, :Ti]), inp.list_ids[b, h, :Ti], L)
+            np.testing.assert_allclose(means[b, h], mu, atol=2e-6, rtol=1e-5)
+            counts = np.bincount(inp.list_ids[b, h, :Ti], minlength=L)
+            assert off[b, h, 0] == 0 and np.array_equal(np.diff(off[b, h]), counts)
+    assert pq.index_dropped(shape, buf) == 0
+
+
+def test_tables_and_keys_match_oracle():
+    import ivf_pq_sparse_amd as pq
+    from oracle import pqhsa_oracle as orc
+    inp = make_step_inputs(1, context_lens=[4000], num_q_heads=8, num_kv_heads=2, num_lists=24,
+                           workload_id=31)
+    g = run_gpu(inp)
+    shape, dec = g["shape"], g["dec"]
+    lay = pq.workspace_layout(shape)
+    ws = dec.workspace
+    G, H, L = 4, 2, 24
+    lut = ws[lay.lut:lay.lut + H * 16 * 256 * G * 4].view(torch.float32).cpu().numpy()
+    lut = lut.reshape(H, 16, 256, G)
+    qc = ws[lay.qc:lay.qc + H * L * G * 4].view(torch.float32).cpu().numpy().reshape(H, L, G)
+    log2e = 1.0 / np.log(2.0)
+    for h in range(H):
+        q = orc.bf16_to_f64(inp.q_bits[0, h * G:(h + 1) * G])
+        qc_ref, lut_ref = orc.lut_tables(q, inp.centroids[0, h].astype(np.float64),
+                                         inp.codebooks[0, h].astype(np.float64), inp.scale)
+        np.testing.assert_allclose(lut[h], np.transpose(lut_ref, (1, 2, 0)) * log2e, atol=2e-6)
+        np.testing.assert_allclose(qc[h], qc_ref.T * log2e, atol=5e-6)
+
+
+def test_repeated_steps_are_deterministic():
+    inp = make_step_inputs(1, context_lens=[20000], num_lists=128, workload_id=40)
+    from pqhsa_synth.device import stage
+    import ivf_pq_sparse_amd as pq
+    tens, kw = stage(inp, "cuda")
+    dec = pq.PQHSADecoder(pq.make_shape(**kw))
+    dec.upload(tens["centroids"], tens["codebooks"], tens["list_ids"], tens["codes"],
+               tens["n_indexed"], tens["v_cache"], tens["block_table"])
+    first = None
+    for _ in range(5):
+        out, sel, _ = dec.step(tens["q"], tens["k_cache"], tens["v_cache"], tens["block_table"],
+                               tens["context_lens"], selected=True)
+        torch.cuda.synchronize()
+        if first is None:
+            first = (out.clone(), sel.clone())
+        else:
+            assert torch.equal(sel, first[1])
+            assert torch.equal(out, first[0])
