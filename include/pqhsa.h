@@ -177,13 +177,13 @@ pqhsa_status pqhsa_dense_decode_step(const pqhsa_shape* shape, const uint16_t* q
                                      float* out, float* lse, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream);
 
-/* Stages of pqhsa_decode_step, in launch order, for profiling. */
+/* Kernels of pqhsa_decode_step, in launch order, for profiling. */
 enum {
   PQHSA_STAGE_TABLES = 0,     /* per-query lookup tables */
   PQHSA_STAGE_SCAN = 1,       /* code scan: approximate logits, keys, cluster bins */
-  PQHSA_STAGE_COLLECT = 2,    /* top-k: threshold bucket and collection */
+  PQHSA_STAGE_COLLECT = 2,    /* top-k: threshold bucket, collection, selected weights */
   PQHSA_STAGE_SELECT = 3,     /* top-k: exact threshold, ascending row list */
-  PQHSA_STAGE_EXACT = 4,      /* paged split-K exact attention + background */
+  PQHSA_STAGE_ATTEND = 4,     /* paged split-K exact attention and background partials */
   PQHSA_STAGE_MERGE = 5,      /* log-sum-exp merge into O */
   PQHSA_NUM_STAGES = 6
 };

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libpqhsa.so")
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "buffer too small",
           4: "HIP error"}
 NUM_STAGES = 6
-STAGE_NAMES = ["tables", "scan", "collect", "select", "exact", "merge"]
+STAGE_NAMES = ["tables", "scan", "collect", "select", "attend", "merge"]
 
 
 class PQHSAError(RuntimeError):

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "pqhsa_internal.hpp"
 
 using namespace pqhsa;
@@ -38,6 +40,7 @@ pqhsa_status validate(const pqhsa_shape* s, bool dense) {
   if (s->budget_bp < 0 || s->budget_bp > 10000) return PQHSA_ERR_INVALID_ARG;
   if (s->num_lists > kMaxLists) return PQHSA_ERR_UNSUPPORTED;
   if (s->pq_m != kM || s->pq_ksub != kKsub) return PQHSA_ERR_UNSUPPORTED;
+  if (s->max_context > kMaxSparseContext) return PQHSA_ERR_UNSUPPORTED;
   return PQHSA_OK;
 }
 
@@ -62,24 +65,39 @@ Dims make_dims(const pqhsa_shape* s, bool dense) {
   d.budget_bp = dense ? 0 : s->budget_bp;
   d.scale_log2 = (float)((double)s->scale * 1.4426950408889634);
   d.nwords = ceil_div(d.cap, 32);
-  d.scan_blocks = ceil_div(d.L, kScanListsPerBlock);
+  {
+    // clusters per scan block: a multiple of its 16 waves, grown until the
+    // grid is about two blocks per CU, so each block's LUT copy into LDS is
+    // amortised over more codes when there are many (b, h)
+    const long long total = (long long)d.B * d.Hkv * d.L;
+    const long long per_wave = (total + kScanWaves * 512LL - 1) / (kScanWaves * 512LL);
+    d.scan_lists = kScanWaves * (int)(per_wave < 1 ? 1 : per_wave);
+    d.scan_blocks = ceil_div(d.L, d.scan_lists);
+  }
   d.collect_slices = ceil_div(d.cap, kCollectEntries);
   d.upload_chunks = ceil_div(d.cap, kUploadChunk);
   if (dense) {
-    d.n_exact_splits = ceil_div(d.cap, kDenseRowsPerSplit);
+    // at least 512 rows per split, and at most 1024 partials per query head
+    const int rows = std::max(kDenseRowsPerSplit, ceil_div(d.cap, 1024));
+    d.n_exact_splits = ceil_div(d.cap, rows);
     d.n_bg_splits = 0;
   } else {
     const long long rows_est = (long long)s->n_sink + s->n_recent + max_selected(s) + 512;
-    int n = ceil_div(rows_est, kExactRowsPerSplit);
-    d.n_exact_splits = n < 1 ? 1 : (n > 4096 ? 4096 : n);
-    d.n_bg_splits = ceil_div(d.L, kBgListsPerBlock);
+    // split counts are rounded up to multiples of 8 so that the blocks of one
+    // (b, h) can all be placed on one XCD
+    d.n_exact_splits = std::min(512, std::max(1, ceil_div(rows_est, kExactRowsPerSplit)));
+    d.n_exact_splits = (d.n_exact_splits + 7) / 8 * 8;
+    // clusters per background wave: batches of 4, at most 256 blocks per (b, h)
+    d.bg_per_wave = kBgBatch * std::max(1, ceil_div(d.L, kBgWaves * kBgBatch * 256));
+    d.n_bg_splits = ceil_div(d.L, kBgWaves * d.bg_per_wave);
+    d.n_bg_splits = (d.n_bg_splits + 7) / 8 * 8;
   }
   d.n_parts = d.n_exact_splits + d.n_bg_splits;
   return d;
 }
 
 struct IndexLayout {
-  size_t centroids, codebooks, list_off, codes, pos, means, n_indexed, dropped, total;
+  size_t centroids, codebooks, list_off, codes, pos, ent_list, means, n_indexed, dropped, total;
 };
 
 IndexLayout index_layout(const Dims& d) {
@@ -91,6 +109,7 @@ IndexLayout index_layout(const Dims& d) {
   l.list_off = o;  o = align_up(o + BH * (d.L + 1) * sizeof(int32_t));
   l.codes = o;     o = align_up(o + BH * d.cap * kM);
   l.pos = o;       o = align_up(o + BH * d.cap * sizeof(int32_t));
+  l.ent_list = o;  o = align_up(o + BH * d.cap * sizeof(int32_t));
   l.means = o;     o = align_up(o + BH * d.L * kD * sizeof(float));
   l.n_indexed = o; o = align_up(o + (size_t)d.B * sizeof(int32_t));
   l.dropped = o;   o = align_up(o + sizeof(unsigned long long));
@@ -99,7 +118,8 @@ IndexLayout index_layout(const Dims& d) {
 }
 
 struct WsLayout {
-  size_t lut, qc, keys, bins, hist, cand_count, cand, sel_p, sel_e, rows, n_rows, partials, total;
+  size_t lut, qc, keys, bins, hist, seg_above, seg_aw, seg_tie, seg_w, seg_cnt, wsel, rows, n_rows,
+      partials, total;
 };
 
 WsLayout ws_layout(const Dims& d, bool dense) {
@@ -113,10 +133,12 @@ WsLayout ws_layout(const Dims& d, bool dense) {
     l.keys = o;       o = align_up(o + BH * d.cap * sizeof(uint32_t));
     l.bins = o;       o = align_up(o + BH * d.L * d.G * 2 * sizeof(float));
     l.hist = o;       o = align_up(o + BH * kHistBins * sizeof(uint32_t));
-    l.cand_count = o; o = align_up(o + BH * sizeof(uint32_t));
-    l.cand = o;       o = align_up(o + BH * d.cap * sizeof(uint4));
-    l.sel_p = o;      o = align_up(o + BH * d.nwords * sizeof(uint32_t));
-    l.sel_e = o;      o = align_up(o + BH * d.nwords * sizeof(uint32_t));
+    l.seg_above = o;  o = align_up(o + BH * d.cap * sizeof(int2));
+    l.seg_aw = o;     o = align_up(o + BH * d.cap * d.G * sizeof(float));
+    l.seg_tie = o;    o = align_up(o + BH * d.cap * sizeof(uint4));
+    l.seg_w = o;      o = align_up(o + BH * d.cap * d.G * sizeof(float));
+    l.seg_cnt = o;    o = align_up(o + BH * d.collect_slices * 2 * sizeof(int32_t));
+    l.wsel = o;       o = align_up(o + BH * d.L * d.G * sizeof(unsigned long long));
     l.rows = o;       o = align_up(o + BH * d.cap * sizeof(int32_t));
     l.n_rows = o;     o = align_up(o + BH * sizeof(int32_t));
   }
@@ -138,6 +160,7 @@ IndexPtrs index_ptrs(const Dims& d, void* buf) {
   ix.list_off = reinterpret_cast<int32_t*>(p + l.list_off);
   ix.codes = reinterpret_cast<uint8_t*>(p + l.codes);
   ix.pos = reinterpret_cast<int32_t*>(p + l.pos);
+  ix.ent_list = reinterpret_cast<int32_t*>(p + l.ent_list);
   ix.means = reinterpret_cast<float*>(p + l.means);
   ix.n_indexed = reinterpret_cast<int32_t*>(p + l.n_indexed);
   ix.dropped = reinterpret_cast<unsigned long long*>(p + l.dropped);
@@ -155,10 +178,12 @@ WsPtrs ws_ptrs(const Dims& d, bool dense, void* buf) {
     w.keys = reinterpret_cast<uint32_t*>(p + l.keys);
     w.bins = reinterpret_cast<float*>(p + l.bins);
     w.hist = reinterpret_cast<uint32_t*>(p + l.hist);
-    w.cand_count = reinterpret_cast<uint32_t*>(p + l.cand_count);
-    w.cand = reinterpret_cast<uint4*>(p + l.cand);
-    w.sel_p = reinterpret_cast<uint32_t*>(p + l.sel_p);
-    w.sel_e = reinterpret_cast<uint32_t*>(p + l.sel_e);
+    w.seg_above = reinterpret_cast<int2*>(p + l.seg_above);
+    w.seg_aw = reinterpret_cast<float*>(p + l.seg_aw);
+    w.seg_tie = reinterpret_cast<uint4*>(p + l.seg_tie);
+    w.seg_w = reinterpret_cast<float*>(p + l.seg_w);
+    w.seg_cnt = reinterpret_cast<int32_t*>(p + l.seg_cnt);
+    w.wsel = reinterpret_cast<unsigned long long*>(p + l.wsel);
     w.rows = reinterpret_cast<int32_t*>(p + l.rows);
     w.n_rows = reinterpret_cast<int32_t*>(p + l.n_rows);
   }
@@ -228,7 +253,7 @@ pqhsa_status run_step(const pqhsa_shape* shape, const void* index_buf, const uin
   PQHSA_TRY(hip_status(launch_collect(a, stream)));
   PQHSA_TRY(record(evs, PQHSA_STAGE_SELECT, stream));
   PQHSA_TRY(hip_status(launch_select(a, stream)));
-  PQHSA_TRY(record(evs, PQHSA_STAGE_EXACT, stream));
+  PQHSA_TRY(record(evs, PQHSA_STAGE_ATTEND, stream));
   PQHSA_TRY(hip_status(launch_exact_and_background(a, false, stream)));
   PQHSA_TRY(record(evs, PQHSA_STAGE_MERGE, stream));
   PQHSA_TRY(hip_status(launch_merge(a, stream)));

@@ -13,11 +13,14 @@
 // honest baseline.
 //
 // Split-K block: 256 threads = 16 row groups of 16 lanes (one DPP row each).
-// A row group reads one token's K and V rows (16 B per lane, 256 B per row),
-// forms the G dot products with a 16-lane DPP reduction and keeps an online
-// base-2 softmax (max, sum, acc[8 dims]) per query head.  Row groups of a
-// wave merge through lane shuffles, the 4 waves through LDS, and the block
-// writes one partial (m, l, acc[128]) per query head.
+// The block first stages the cache offsets of up to 256 rows in LDS (row list
+// and block table read once, in parallel); each row group then streams its
+// rows with the next two rows' K and V (16 B per lane, 256 B per row) in
+// flight while it computes the current two: the G dot products use a 16-lane
+// DPP reduction, and an online base-2 softmax (max, sum, acc[8 dims]) is kept
+// per query head.  Row groups of a wave merge through lane shuffles, the 4
+// waves through LDS, and the block writes one partial (m, l, acc[128]) per
+// query head.
 #include "pqhsa_internal.hpp"
 
 namespace pqhsa {
@@ -50,35 +53,26 @@ __device__ __forceinline__ void attend_row(AttnState<G>& st, const float (&qv)[G
   }
 }
 
-// Merge (m1, w1) into (m0, w0) style states: returns the two scale factors.
+// Scale factors that bring states with maxima m0 and m1 to their common max.
 __device__ __forceinline__ void lse_factors(float m0, float m1, float* M, float* a0, float* a1) {
   *M = fmaxf(m0, m1);
   *a0 = (m0 == -INFINITY) ? 0.0f : exp2f(m0 - *M);
   *a1 = (m1 == -INFINITY) ? 0.0f : exp2f(m1 - *M);
 }
 
-// LDS scratch of the block-level merge: 4 waves x G heads x (m, l, acc[128]).
+// LDS of one attend block: staged row offsets, then the merge of 4 waves x G
+// heads x (m, l, acc[128]).
 template <int G>
-struct MergeLds {
+struct AttendLds {
+  long long row_off[kPhaseRows];
   float ml[4][G][2];
   float acc[4][G][kD];
 };
 
-// Write (m, l, acc) of the 4 waves' lanes 0..15 (8 dims each) to LDS, merge
-// and store one partial per query head at `slot`.
+// Merge the per-wave states held in LDS (ml, acc) and store one partial per
+// query head at `slot`.
 template <int G>
-__device__ void block_merge_store(MergeLds<G>& sh, const float* m, const float* l,
-                                  const float (*acc)[8], int l16, bool writer, float* part_base,
-                                  int n_parts, int slot) {
-  const int wave = threadIdx.x >> 6;
-  if (writer) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (l16 == 0) { sh.ml[wave][g][0] = m[g]; sh.ml[wave][g][1] = l[g]; }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sh.acc[wave][g][l16 * 8 + i] = acc[g][i];
-    }
-  }
+__device__ void block_merge_store(AttendLds<G>& sh, float* part_base, int n_parts, int slot) {
   __syncthreads();
   for (int idx = threadIdx.x; idx < G * kD; idx += blockDim.x) {
     const int g = idx / kD, dim = idx % kD;
@@ -104,14 +98,14 @@ __device__ void block_merge_store(MergeLds<G>& sh, const float* m, const float* 
 // Split-K exact attention for one (b, h, split): rows [r0, r1) of either the
 // index-list row array (DENSE = false) or the whole context (DENSE = true).
 template <int G, bool DENSE>
-__device__ void exact_block(const StepArgs& a, int bh, int split, MergeLds<G>& sh) {
+__device__ void exact_block(const StepArgs& a, int bh, int split, AttendLds<G>& sh) {
   const Dims& d = a.d;
   const int b = bh / d.Hkv, h = bh % d.Hkv;
   const int l16 = threadIdx.x & 15;
   const int rg = threadIdx.x >> 4;
   int n_rows;
   if constexpr (DENSE) n_rows = min(max(a.ctx[b], 0), d.cap);
-  else n_rows = a.ws.n_rows[bh];
+  else n_rows = min(max(a.ws.n_rows[bh], 0), d.cap);
   const int chunk = (n_rows + d.n_exact_splits - 1) / d.n_exact_splits;
   const int r0 = min(n_rows, split * chunk);
   const int r1 = min(n_rows, r0 + chunk);
@@ -137,29 +131,50 @@ __device__ void exact_block(const StepArgs& a, int bh, int split, MergeLds<G>& s
     for (int i = 0; i < 8; ++i) st.acc[g][i] = 0.0f;
   }
   const int32_t* tab = a.table + (size_t)b * d.max_pages;
-  const int32_t* rows = DENSE ? nullptr : a.ws.rows + (size_t)bh * d.cap;
-  auto row_offset = [&](int r) -> size_t {
-    const int p = DENSE ? r : rows[r];
-    int page = tab[p >> 4];
-    page = min(max(page, 0), d.num_pages - 1);
-    return ((size_t)(page * kPage + (p & (kPage - 1))) * d.Hkv + h) * kD + l16 * 8;
-  };
-  int r = r0 + rg;
-  // two rows per step so that four 16-byte loads per lane are in flight
-  for (; r + 16 < r1; r += 32) {
-    const size_t o0 = row_offset(r), o1 = row_offset(r + 16);
-    const uint4 k0 = *reinterpret_cast<const uint4*>(a.kc + o0);
-    const uint4 v0 = *reinterpret_cast<const uint4*>(a.vc + o0);
-    const uint4 k1 = *reinterpret_cast<const uint4*>(a.kc + o1);
-    const uint4 v1 = *reinterpret_cast<const uint4*>(a.vc + o1);
-    attend_row<G>(st, qv, k0, v0);
-    attend_row<G>(st, qv, k1, v1);
-  }
-  if (r < r1) {
-    const size_t o0 = row_offset(r);
-    const uint4 k0 = *reinterpret_cast<const uint4*>(a.kc + o0);
-    const uint4 v0 = *reinterpret_cast<const uint4*>(a.vc + o0);
-    attend_row<G>(st, qv, k0, v0);
+  const int32_t* rows = a.ws.rows + (size_t)bh * d.cap;
+  const uint16_t* kc = a.kc + l16 * 8;
+  const uint16_t* vc = a.vc + l16 * 8;
+  for (int ph = r0; ph < r1; ph += kPhaseRows) {
+    const int n = min(kPhaseRows, r1 - ph);
+    if ((int)threadIdx.x < n) {
+      const int p = DENSE ? ph + (int)threadIdx.x : min(max(rows[ph + threadIdx.x], 0), d.cap - 1);
+      int page = tab[p >> 4];
+      page = min(max(page, 0), d.num_pages - 1);
+      sh.row_off[threadIdx.x] =
+          ((long long)(page * kPage + (p & (kPage - 1))) * d.Hkv + h) * kD;
+    }
+    __syncthreads();
+    int j = rg;
+    uint4 k0 = make_uint4(0, 0, 0, 0), v0 = k0, k1 = k0, v1 = k0;
+    if (j < n) {
+      const long long o = sh.row_off[j];
+      k0 = *reinterpret_cast<const uint4*>(kc + o);
+      v0 = *reinterpret_cast<const uint4*>(vc + o);
+    }
+    if (j + 16 < n) {
+      const long long o = sh.row_off[j + 16];
+      k1 = *reinterpret_cast<const uint4*>(kc + o);
+      v1 = *reinterpret_cast<const uint4*>(vc + o);
+    }
+    while (j < n) {
+      const int jn = j + 32;
+      uint4 nk0 = k0, nv0 = v0, nk1 = k1, nv1 = v1;
+      if (jn < n) {
+        const long long o = sh.row_off[jn];
+        nk0 = *reinterpret_cast<const uint4*>(kc + o);
+        nv0 = *reinterpret_cast<const uint4*>(vc + o);
+      }
+      if (jn + 16 < n) {
+        const long long o = sh.row_off[jn + 16];
+        nk1 = *reinterpret_cast<const uint4*>(kc + o);
+        nv1 = *reinterpret_cast<const uint4*>(vc + o);
+      }
+      attend_row<G>(st, qv, k0, v0);
+      if (j + 16 < n) attend_row<G>(st, qv, k1, v1);
+      k0 = nk0; v0 = nv0; k1 = nk1; v1 = nv1;
+      j = jn;
+    }
+    __syncthreads();
   }
   // merge the wave's 4 row groups (lanes l, l^16, l^32, l^48 hold the same dims)
 #pragma unroll
@@ -179,70 +194,77 @@ __device__ void exact_block(const StepArgs& a, int bh, int split, MergeLds<G>& s
       st.m[g] = M;
     }
   }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) < 16) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (l16 == 0) { sh.ml[wave][g][0] = st.m[g]; sh.ml[wave][g][1] = st.l[g]; }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sh.acc[wave][g][l16 * 8 + i] = st.acc[g][i];
+    }
+  }
   float* part_base = a.ws.partials + ((size_t)b * d.Hq + h * G) * d.n_parts * kPart;
-  block_merge_store<G>(sh, st.m, st.l, st.acc, l16, (threadIdx.x & 63) < 16, part_base,
-                       d.n_parts, split);
+  block_merge_store<G>(sh, part_base, d.n_parts, split);
 }
 
-// Background partial for clusters [c0, c1) of (b, h): per cluster the
-// candidates' summed weight minus the selected ones' weight, times the mean.
+// Background partial for the clusters of one (b, h, split): per cluster the
+// candidates' summed weight minus the selected ones', times the cluster mean.
+// Wave w handles bg_per_wave consecutive clusters in batches of 4 whose loads
+// are issued together.
 template <int G>
-__device__ void background_block(const StepArgs& a, int bh, int split, MergeLds<G>& sh) {
+__device__ void background_block(const StepArgs& a, int bh, int split, AttendLds<G>& sh) {
+  constexpr int NB = kBgBatch;
   const Dims& d = a.d;
   const int b = bh / d.Hkv, h = bh % d.Hkv;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int per = (d.L + d.n_bg_splits - 1) / d.n_bg_splits;
-  const int c0 = min(d.L, split * per), c1 = min(d.L, c0 + per);
-  const int32_t* off = a.ix.list_off + (size_t)bh * (d.L + 1);
-  const uint4* codes = reinterpret_cast<const uint4*>(a.ix.codes + (size_t)bh * d.cap * kM);
-  const uint32_t* sel_e = a.ws.sel_e + (size_t)bh * d.nwords;
-  const float* lut = a.ws.lut + (size_t)bh * kM * kKsub * G;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cw0 = (split * kBgWaves + wave) * d.bg_per_wave;
+  const int cw1 = min(d.L, cw0 + d.bg_per_wave);
   float M[G], Lw[G], acc[G][2];
 #pragma unroll
-  for (int g = 0; g < G; ++g) { M[g] = -INFINITY; Lw[g] = 0.0f; acc[g][0] = acc[g][1] = 0.0f; }
-  for (int c = c0 + wave; c < c1; c += 4) {
-    const float* bin = a.ws.bins + ((size_t)bh * d.L + c) * G * 2;
-    float Mc[G], Wc[G], qc[G];
-    bool any = false;
+  for (int g = 0; g < G; ++g) {
+    M[g] = -INFINITY;
+    Lw[g] = 0.0f;
+    acc[g][0] = acc[g][1] = 0.0f;
+  }
+  for (int cb = cw0; cb < cw1; cb += NB) {
+    float2 mu[NB];
+    float Mc[NB][G], Wc[NB][G];
+    unsigned long long Ws[NB][G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      Mc[g] = bin[2 * g];
-      Wc[g] = bin[2 * g + 1];
-      qc[g] = a.ws.qc[((size_t)bh * d.L + c) * G + g];
-      any |= Wc[g] > 0.0f;
-    }
-    if (!any) continue;
-    const int e1 = min(off[c + 1], d.cap), e0 = min(max(off[c], 0), e1);
-    float wsel[G];
+    for (int i = 0; i < NB; ++i) {
+      const int c = cb + i;
+      mu[i] = make_float2(0.0f, 0.0f);
 #pragma unroll
-    for (int g = 0; g < G; ++g) wsel[g] = 0.0f;
-    for (int eb = e0; eb < e1; eb += 64) {
-      const int e = eb + lane;
-      bool sel = false;
-      if (e < e1) sel = (sel_e[e >> 5] >> (e & 31)) & 1u;
-      if (sel) {
-        float s[G];
-        entry_logits<G>(lut, qc, codes[e], s);
+      for (int g = 0; g < G; ++g) { Mc[i][g] = -INFINITY; Wc[i][g] = 0.0f; Ws[i][g] = 0ull; }
+      if (c < cw1) {
+        mu[i] = *reinterpret_cast<const float2*>(a.ix.means + ((size_t)bh * d.L + c) * kD + 2 * lane);
+        const float* bin = a.ws.bins + ((size_t)bh * d.L + c) * G * 2;
+        const unsigned long long* ws = a.ws.wsel + ((size_t)bh * d.L + c) * G;
 #pragma unroll
-        for (int g = 0; g < G; ++g) wsel[g] += exp2f(s[g] - Mc[g]);
+        for (int g = 0; g < G; ++g) {
+          Mc[i][g] = bin[2 * g];
+          Wc[i][g] = bin[2 * g + 1];
+          Ws[i][g] = ws[g];
+        }
       }
     }
-    const float2 mu = *reinterpret_cast<const float2*>(a.ix.means + ((size_t)bh * d.L + c) * kD + 2 * lane);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float wb = fmaxf(Wc[g] - wave_sum(wsel[g]), 0.0f);
-      if (wb > 0.0f) {
-        float Mn, f0, f1;
-        lse_factors(M[g], Mc[g], &Mn, &f0, &f1);
-        const float w = f1 * wb;
-        Lw[g] = fmaf(Lw[g], f0, w);
-        acc[g][0] = fmaf(acc[g][0], f0, w * mu.x);
-        acc[g][1] = fmaf(acc[g][1], f0, w * mu.y);
-        M[g] = Mn;
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const float wb = fmaxf(Wc[i][g] - (float)Ws[i][g] * kFixInv, 0.0f);
+        if (wb > 0.0f) {
+          float Mn, f0, f1;
+          lse_factors(M[g], Mc[i][g], &Mn, &f0, &f1);
+          const float w = f1 * wb;
+          Lw[g] = fmaf(Lw[g], f0, w);
+          acc[g][0] = fmaf(acc[g][0], f0, w * mu[i].x);
+          acc[g][1] = fmaf(acc[g][1], f0, w * mu[i].y);
+          M[g] = Mn;
+        }
       }
     }
   }
-  // store through the same LDS merge: lanes hold dims (2*lane, 2*lane+1)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     if (lane == 0) { sh.ml[wave][g][0] = M[g]; sh.ml[wave][g][1] = Lw[g]; }
@@ -250,47 +272,87 @@ __device__ void background_block(const StepArgs& a, int bh, int split, MergeLds<
     sh.acc[wave][g][2 * lane + 1] = acc[g][1];
   }
   float* part_base = a.ws.partials + ((size_t)b * d.Hq + h * G) * d.n_parts * kPart;
-  // writer=false: LDS already filled above
-  const float dummy_acc[G][8] = {};
-  block_merge_store<G>(sh, M, Lw, dummy_acc, 0, false, part_base, d.n_parts,
-                       d.n_exact_splits + split);
+  block_merge_store<G>(sh, part_base, d.n_parts, d.n_exact_splits + split);
 }
 
 // One launch for both: blocks [0, BH*n_exact) do split-K, the rest background.
 template <int G, bool DENSE>
 __global__ __launch_bounds__(256) void k_attend(StepArgs a) {
-  __shared__ MergeLds<G> sh;
+  __shared__ AttendLds<G> sh;
   const int BH = a.d.B * a.d.Hkv;
   const int n_exact_blocks = BH * a.d.n_exact_splits;
   const int blk = blockIdx.x;
+  int bh, sub;
   if (blk < n_exact_blocks) {
-    exact_block<G, DENSE>(a, blk / a.d.n_exact_splits, blk % a.d.n_exact_splits, sh);
+    xcd_map(blk, BH, a.d.n_exact_splits, &bh, &sub);
+    exact_block<G, DENSE>(a, bh, sub, sh);
   } else if constexpr (!DENSE) {
-    const int i = blk - n_exact_blocks;
-    background_block<G>(a, i / a.d.n_bg_splits, i % a.d.n_bg_splits, sh);
+    xcd_map(blk - n_exact_blocks, BH, a.d.n_bg_splits, &bh, &sub);
+    background_block<G>(a, bh, sub, sh);
   }
 }
 
-// grid (B*Hq), 128 threads (one per output dim).
-__global__ __launch_bounds__(128) void k_merge(StepArgs a) {
-  const int bq = blockIdx.x;
-  const int dim = threadIdx.x;
+// Log-sum-exp merge of one query head's n_parts partials into O and the
+// log-sum-exp.  grid (B*Hq), 256 threads = 2 halves of the parts x 128 dims.
+// The parts' maxima and sums are staged in LDS; each thread then sums its dim
+// over its half of the parts, issuing 16 loads before using any.
+__global__ __launch_bounds__(256) void k_merge(StepArgs a) {
+  extern __shared__ float mlds[];   // [np] weights, [np] sums, [128] second half's sums
+  __shared__ float red[8];
   const int np = a.d.n_parts;
-  const float* p = a.ws.partials + (size_t)bq * np * kPart;
-  float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, p[(size_t)i * kPart]);
-  float L = 0.0f, A = 0.0f;
-  if (M != -INFINITY) {
-#pragma unroll 4
-    for (int i = 0; i < np; ++i) {
-      const float mi = p[(size_t)i * kPart];
-      const float f = (mi == -INFINITY) ? 0.0f : exp2f(mi - M);
-      L = fmaf(f, p[(size_t)i * kPart + 1], L);
-      A = fmaf(f, p[(size_t)i * kPart + 4 + dim], A);
-    }
+  const int G = a.d.G;
+  int bh, g;
+  xcd_map(blockIdx.x, a.d.B * a.d.Hkv, G, &bh, &g);
+  const int bq = (bh / a.d.Hkv) * a.d.Hq + (bh % a.d.Hkv) * G + g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* part = a.ws.partials + (size_t)bq * np * kPart;
+  float* wts = mlds;
+  float* ls = mlds + np;
+  float* half1 = mlds + 2 * np;
+  float mx = -INFINITY;
+  for (int i = tid; i < np; i += blockDim.x) {
+    const float m = part[(size_t)i * kPart];
+    wts[i] = m;
+    ls[i] = part[(size_t)i * kPart + 1];
+    mx = fmaxf(mx, m);
   }
-  a.out[(size_t)bq * kD + dim] = L > 0.0f ? A / L : 0.0f;
-  if (dim == 0 && a.lse) a.lse[bq] = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float lsum = 0.0f;
+  for (int i = tid; i < np; i += blockDim.x) {
+    const float m = wts[i];
+    const float f = (m == -INFINITY || M == -INFINITY) ? 0.0f : exp2f(m - M);
+    wts[i] = f;
+    lsum = fmaf(f, ls[i], lsum);
+  }
+  lsum = wave_sum(lsum);
+  __syncthreads();
+  if (lane == 0) red[4 + wave] = lsum;
+  __syncthreads();
+  const float L = (red[4] + red[5]) + (red[6] + red[7]);
+  const int dim = tid & (kD - 1), half = tid >> 7;
+  const int hp = (np + 1) / 2;
+  const int i0 = half * hp, i1 = min(np, i0 + hp);
+  const float* pd = part + 4 + dim;
+  float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = i0; i < i1; i += 16) {
+    float x[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) x[u] = (i + u < i1) ? pd[(size_t)(i + u) * kPart] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (i + u < i1) A[u & 3] = fmaf(wts[i + u], x[u], A[u & 3]);
+  }
+  const float sum = (A[0] + A[1]) + (A[2] + A[3]);
+  if (half == 1) half1[dim] = sum;
+  __syncthreads();
+  if (half == 0) {
+    const float tot = sum + half1[dim];
+    a.out[(size_t)bq * kD + dim] = L > 0.0f ? tot / L : 0.0f;
+    if (dim == 0 && a.lse) a.lse[bq] = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+  }
 }
 
 template <int G>
@@ -305,18 +367,25 @@ static hipError_t attend_g(const StepArgs& a, bool dense, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_exact_and_background(const StepArgs& a, bool dense, hipStream_t st) {
-  switch (a.d.G) {
-    case 1: return attend_g<1>(a, dense, st);
-    case 2: return attend_g<2>(a, dense, st);
-    case 4: return attend_g<4>(a, dense, st);
-    case 8: return attend_g<8>(a, dense, st);
-  }
+#define PQHSA_G_DISPATCH2(fn, ...)                  \
+  switch (a.d.G) {                                  \
+    case 1: return fn<1>(__VA_ARGS__);              \
+    case 2: return fn<2>(__VA_ARGS__);              \
+    case 4: return fn<4>(__VA_ARGS__);              \
+    case 8: return fn<8>(__VA_ARGS__);              \
+  }                                                 \
   return hipErrorInvalidValue;
+
+hipError_t launch_exact_and_background(const StepArgs& a, bool dense, hipStream_t st) {
+  PQHSA_G_DISPATCH2(attend_g, a, dense, st)
 }
 
 hipError_t launch_merge(const StepArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_merge, dim3(a.d.B * a.d.Hq), dim3(128), 0, st, a);
+  const size_t lds = ((size_t)2 * a.d.n_parts + kD) * sizeof(float);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_merge),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_merge, dim3(a.d.B * a.d.Hq), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 

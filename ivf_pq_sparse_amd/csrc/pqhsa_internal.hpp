@@ -19,13 +19,22 @@ constexpr int kHistBins = 1 << kHistBits;
 constexpr int kPart = 132;       // floats per partial: m (base 2), l, pad, pad, acc[128]
 constexpr int kMaxLists = 16384;
 constexpr int kScanThreads = 1024;
-constexpr int kScanListsPerBlock = 16;
-constexpr int kCollectEntries = 4096;   // index entries per collect block
+constexpr int kScanWaves = kScanThreads / 64;
+constexpr int kScanPrefetch = 4;         // 64-entry tiles in flight per wave
+constexpr int kCollectThreads = 256;
+constexpr int kCollectPerThread = 16;
+constexpr int kCollectEntries = kCollectThreads * kCollectPerThread;  // entries per collect block
+constexpr int kSelectThreads = 512;
+constexpr int kMaxSparseContext = 1 << 20;  // position bitmap of the selection lives in LDS
 constexpr int kExactRowsPerSplit = 64;  // target rows per split-K block (index-list mode)
 constexpr int kDenseRowsPerSplit = 512; // rows per split-K block (dense mode)
-constexpr int kBgListsPerBlock = 64;
+constexpr int kPhaseRows = 256;         // rows whose cache offsets are staged in LDS at once
+constexpr int kBgWaves = 4;             // waves per background block
+constexpr int kBgBatch = 4;             // clusters whose loads a background wave issues together
 constexpr int kUploadChunk = 4096;      // tokens per counting-sort chunk
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kFixScale = 1099511627776.0f;   // 2^40: fixed-point unit of selected weights
+constexpr float kFixInv = 1.0f / 1099511627776.0f;
 
 // Shape-derived sizes, passed to every kernel by value.
 struct Dims {
@@ -34,9 +43,11 @@ struct Dims {
   float scale_log2;           // scale * log2(e): logits are kept in base 2
   int nwords;                 // ceil(cap / 32): words of a per-head bitmap
   int scan_blocks;            // scan blocks per (b, h)
+  int scan_lists;             // clusters per scan block (a multiple of its 16 waves)
   int collect_slices;         // collect blocks per (b, h)
   int n_exact_splits;         // split-K blocks per (b, h)
   int n_bg_splits;            // background blocks per (b, h)
+  int bg_per_wave;            // clusters per background wave (a multiple of 4)
   int n_parts;                // partials per (b, q head)
   int upload_chunks;          // counting-sort chunks per (b, h)
 };
@@ -47,6 +58,7 @@ struct IndexPtrs {
   int32_t* list_off;   // [BH][L+1]
   uint8_t* codes;      // [BH][cap][16] cluster order
   int32_t* pos;        // [BH][cap]     token position of each entry
+  int32_t* ent_list;   // [BH][cap]     cluster of each entry
   float* means;        // [BH][L][128]
   int32_t* n_indexed;  // [B]
   unsigned long long* dropped;  // [1]
@@ -58,11 +70,15 @@ struct WsPtrs {
   uint32_t* keys;      // [BH][cap]
   float* bins;         // [BH][L][G][2]
   uint32_t* hist;      // [BH][4096]
-  uint32_t* cand_count;// [BH]
-  uint4* cand;         // [BH][cap]  (key, pos, entry, 0)
-  uint32_t* sel_p;     // [BH][nwords] bitmap over positions
-  uint32_t* sel_e;     // [BH][nwords] bitmap over index entries
-  int32_t* rows;       // [BH][cap]
+  int2* seg_above;     // [BH][cap]  (pos, cluster) of keys above the threshold bucket,
+                       //            one 4096-slot segment per collect block
+  float* seg_aw;       // [BH][cap][G] their approximate weights relative to the cluster max
+  uint4* seg_tie;      // [BH][cap]  (key, pos, entry, cluster) of keys in the threshold bucket
+  float* seg_w;        // [BH][cap][G] their approximate weights relative to the cluster max
+  int32_t* seg_cnt;    // [BH][slices][2] counts (above, tie) of each segment
+  unsigned long long* wsel;  // [BH][L][G] selected entries' weights per cluster, fixed point 2^-40
+                             // (written by the selection with plain stores)
+  int32_t* rows;       // [BH][cap] exact rows as physical cache rows (page * 16 + slot)
   int32_t* n_rows;     // [BH]
   float* partials;     // [B][Hq][n_parts][132]
 };
@@ -127,6 +143,30 @@ __device__ __forceinline__ float wave_sum(float x) {
 __device__ __forceinline__ float wave_max(float x) {
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
   return x;
+}
+
+// Block index -> (b*Hkv + h, sub-block) so that every kernel runs all blocks
+// of one (b, h) on the same XCD: workgroups go to the 8 XCDs round-robin by
+// linear index, and each XCD has its own L2, so a consumer kernel then finds
+// its producer's data in the same L2.  `per` blocks per (b, h), BH heads.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void xcd_map(int x, int BH, int per, int* bh, int* sub) {
+  const int total = BH * per;
+  if (total % kXcds == 0) {
+    const int xcd = x % kXcds, j = x / kXcds;
+    if (BH % kXcds == 0) {
+      *bh = xcd + kXcds * (j / per);
+      *sub = j % per;
+      return;
+    }
+    if (kXcds % BH == 0) {
+      *bh = xcd % BH;
+      *sub = xcd / BH + (kXcds / BH) * j;
+      return;
+    }
+  }
+  *bh = x / per;
+  *sub = x % per;
 }
 
 // Per-sequence quantities of the forced/candidate split.

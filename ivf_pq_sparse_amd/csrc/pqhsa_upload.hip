@@ -108,6 +108,7 @@ __global__ __launch_bounds__(64) void k_upload_scatter(UploadArgs a) {
   const uint4* codes_in = reinterpret_cast<const uint4*>(a.codes + (size_t)bh * d.cap * kM);
   uint4* codes_out = reinterpret_cast<uint4*>(a.ix.codes + (size_t)bh * d.cap * kM);
   int32_t* pos_out = a.ix.pos + (size_t)bh * d.cap;
+  int32_t* list_out = a.ix.ent_list + (size_t)bh * d.cap;
   __syncthreads();
   for (int s = t0; s < t1; s += 64) {
     const int t = s + lane;
@@ -128,6 +129,7 @@ __global__ __launch_bounds__(64) void k_upload_scatter(UploadArgs a) {
       const int dest = base[c] + rank;
       codes_out[dest] = codes_in[t];
       pos_out[dest] = t;
+      list_out[dest] = c;
     }
     __syncthreads();
     if (c >= 0 && rank == same - 1) base[c] += same;

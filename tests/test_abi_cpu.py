@@ -61,9 +61,10 @@ def test_sizes_for_the_128k_layer(shape):
     import ivf_pq_sparse_amd as pq
     assert pq.max_selected(shape) == 1311
     ib = pq.index_bytes(shape)
-    # codes 16 B + position 4 B per token and head, centroids, means, codebooks
+    # codes 16 B + position 4 B + cluster id 4 B per token and head,
+    # centroids, means, codebooks
     BH, cap, L = 8, 131072, 512
-    floor = BH * cap * 20 + BH * L * 128 * 4 * 2 + BH * 16 * 256 * 8 * 4
+    floor = BH * cap * 24 + BH * L * 128 * 4 * 2 + BH * 16 * 256 * 8 * 4
     assert floor <= ib <= floor + 64 * 1024
     ws = pq.workspace_bytes(shape)
     lay = pq.workspace_layout(shape)
@@ -97,6 +98,16 @@ def test_invalid_shapes_are_rejected(lib, shape, field, value, expect):
     st = lib.pqhsa_upload_index(ctypes.byref(shape), fake, fake, fake, fake, fake, fake, fake,
                                 fake, 1 << 40, fake, 1 << 40, None)
     assert st == expect
+
+
+def test_sparse_context_limit(lib, shape):
+    import ivf_pq_sparse_amd as pq
+    shape.max_pages_per_seq = 1 << 17
+    shape.max_context = (1 << 20) + 16       # above the selection bitmap held in LDS
+    assert pq.workspace_bytes(shape) == 0 and pq.index_bytes(shape) == 0
+    assert pq.workspace_bytes(shape, dense=True) > 0     # the dense path has no such limit
+    shape.max_context = 1 << 20
+    assert pq.workspace_bytes(shape) > 0
 
 
 def test_dense_ignores_method_fields(lib, shape):
