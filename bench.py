@@ -46,32 +46,173 @@ def parse():
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain device copy of known size (for counter scaling)")
+    p.add_argument("--summarize-profile", nargs=4, metavar=("TRACE", "FETCH", "WRITE", "OUT"),
+                   help="write the markdown summary of three rocprofv3 output folders and exit")
+    p.add_argument("--profile-command", default="",
+                   help="the command line recorded in the summary")
     return p.parse_args()
 
 
-def algorithmic_bytes(inp, n_rows_per_head, k_sel):
-    """Bytes the method must move per step (per stage and in total).
+def algorithmic_bytes(inp, n_rows_per_head, k_sel, n_parts):
+    """Bytes the method must move per step: in total (the step) and per kernel.
 
-    scan:   per indexed entry 16 B codes + 4 B position read, 4 B key written;
-            per (b, h) the lookup table and cluster tables.
-    exact:  512 B (bf16 K + V row) per exact row, 4 B row index.
-    background: cluster means (512 B per cluster), bins, selected codes.
+    Step total (the method's own data, scratch not counted): per indexed token
+    and KV head 16 B of PQ codes and a 2 B list id; 512 B of bf16 K+V per
+    exactly attended row; per KV head the fp32 cluster means and centroids
+    (512 B per cluster each) and codebooks (16*256*8*4 B); q and O.
+
+    Per kernel (what one launch must read and write at least, scratch
+    included, each array once):
+      tables:  q, codebooks, centroids; writes LUT (16*256*G*4 B) and QC (L*G*4 B)
+      scan:    per indexed entry 16 B codes + 4 B position read and a 4 B key
+               written; per head LUT + QC read, cluster bins (L*G*8 B) written
+      collect: per indexed entry the 4 B key; per head the 16 KB histogram;
+               writes (position, cluster, G weights) of the k chosen entries
+      select:  reads those k records; writes the exact row list (4 B per row),
+               the selected positions (4 B each) and selected weights (L*G*8 B)
+      attend:  512 B K+V + 4 B row id per exact row; per head the means
+               (L*512 B), bins and selected weights; writes the partials
+      merge:   reads the partials (132*4 B each), writes O (512 B per q head)
     """
     B, Hkv, Hq = inp.batch, inp.num_kv_heads, inp.num_q_heads
     G, L = Hq // Hkv, inp.num_lists
+    BH = B * Hkv
     n_idx = int(np.sum(inp.n_indexed)) * Hkv
-    per_head_tables = 16 * 256 * G * 4 + L * G * 4 + L * G * 8
-    scan = n_idx * (16 + 4 + 4) + B * Hkv * per_head_tables
-    exact = int(n_rows_per_head.sum()) * (512 + 4)
-    background = B * Hkv * (L * 512 + L * G * 8 + L * G * 4) + int(k_sel.sum()) * 16
-    tables = B * Hkv * (16 * 256 * 8 * 4 + L * 128 * 4 + per_head_tables) + B * Hq * 256
-    io = B * Hq * 128 * 4
-    total = scan + exact + background + tables + io
-    return dict(scan=scan, exact=exact, background=background, tables=tables, total=total)
+    rows = int(n_rows_per_head.sum())
+    ksum = int(k_sel.sum())
+    lut, qc, bins = 16 * 256 * G * 4, L * G * 4, L * G * 8
+    partials = B * Hq * n_parts * 132 * 4
+    rec = 8 + 4 * G
+    k = {
+        "tables": B * Hq * 256 + BH * (16 * 256 * 8 * 4 + L * 512 + lut + qc),
+        "scan": n_idx * (16 + 4 + 4) + BH * (lut + qc + bins + (L + 1) * 4),
+        "collect": n_idx * 4 + BH * 4096 * 4 + ksum * rec,
+        "select": ksum * rec + rows * 4 + ksum * 4 + BH * bins,
+        "attend": rows * (512 + 4) + BH * (L * 512 + 2 * bins) + partials,
+        "merge": partials + B * Hq * 512,
+    }
+    total = (n_idx * 18 + rows * 512 + BH * (2 * L * 512 + 16 * 256 * 8 * 4)
+             + B * Hq * 128 * (2 + 4))
+    return total, k
+
+
+# ------------------------------------------------------------------ counters
+def source_digest():
+    """SHA-256 over the kernel sources: counter figures are valid only for the
+    sources they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "ivf_pq_sparse_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "pqhsa.h"), "rb").read())
+    return h.hexdigest()
+
+
+def _short_kernel(name):
+    base = name.split("(")[0].replace("void ", "")
+    if base.startswith("pqhsa::"):
+        base = base[len("pqhsa::"):]
+    return base.replace(" ", "")
+
+
+def summarize_profile(trace_dir, fetch_dir, write_dir, out, command):
+    """Write the markdown summary of one rocprofv3 kernel-trace run and two
+    counter runs (FETCH_SIZE, WRITE_SIZE) of the same bench command.  The
+    counters are scaled by what they read for the largest plain device copy
+    in the run (`--copy-calibration`: 1 GiB read, 1 GiB written)."""
+    import csv
+    import glob
+
+    def rows(d, pat):
+        f = glob.glob(os.path.join(d, pat))
+        if not f:
+            raise SystemExit(f"no {pat} under {d}")
+        return list(csv.DictReader(open(f[0])))
+
+    stats = rows(trace_dir, "*kernel_stats.csv")
+    counters = {}
+    copy_kib = {}
+    for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        per = {}
+        for r in rows(d, "*counter_collection.csv"):
+            if r["Counter_Name"] != cname:
+                continue
+            v = float(r["Counter_Value"])
+            if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer"):
+                copy_kib[cname] = max(copy_kib.get(cname, 0.0), v)
+            per.setdefault(_short_kernel(r["Kernel_Name"]), []).append(v)
+        counters[cname] = {k: (float(np.mean(v)), len(v)) for k, v in per.items()}
+    gib_kib = float(1 << 20)
+    scale = {c: gib_kib / copy_kib[c] for c in copy_kib}
+    lines = ["# rocprofv3 summary: PQ-HSA decode step kernels", "",
+             "Command (run from the repository root; three runs of the same bench command):", "",
+             "```", command, "```", "",
+             f"source_sha256: {source_digest()}", "",
+             "Copy calibration (largest `__amd_rocclr_copyBuffer` dispatch, 1 GiB read + 1 GiB "
+             "written):", ""]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        if c in copy_kib:
+            lines.append(f"- {c}: {copy_kib[c]:.1f} KiB counted for {gib_kib:.0f} KiB moved: "
+                         f"scale x{scale[c]:.4f}")
+    lines += ["", "| kernel | calls | avg ns | min ns | max ns | FETCH KiB/dispatch | "
+              "WRITE KiB/dispatch | scaled MB/dispatch (read + write) |",
+              "|---|---|---|---|---|---|---|---|"]
+    for r in stats:
+        k = _short_kernel(r["Name"])
+        if not (k.startswith("k_") or k.startswith("__amd_rocclr_copyBuffer")):
+            continue
+        f = counters.get("FETCH_SIZE", {}).get(k)
+        w = counters.get("WRITE_SIZE", {}).get(k)
+        mb = ""
+        if f and w and "FETCH_SIZE" in scale and "WRITE_SIZE" in scale:
+            mb = f"{(f[0] * scale['FETCH_SIZE'] + w[0] * scale['WRITE_SIZE']) * 1024 / 1e6:.3f}"
+        lines.append(f"| {k} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                     f"{r['MaxNs']} | {f[0] if f else float('nan'):.1f} | "
+                     f"{w[0] if w else float('nan'):.1f} | {mb} |")
+    lines += ["", "Machine-readable (kernel, avg_ns, scaled_bytes_per_dispatch):", "", "```"]
+    for r in stats:
+        k = _short_kernel(r["Name"])
+        f = counters.get("FETCH_SIZE", {}).get(k)
+        w = counters.get("WRITE_SIZE", {}).get(k)
+        if k.startswith("k_") and f and w and "FETCH_SIZE" in scale and "WRITE_SIZE" in scale:
+            b = (f[0] * scale["FETCH_SIZE"] + w[0] * scale["WRITE_SIZE"]) * 1024
+            lines.append(f"{k} {float(r['AverageNs']):.0f} {b:.0f}")
+    lines += ["```", ""]
+    open(out, "w").write("\n".join(lines))
+    print(f"wrote {out}", file=sys.stderr)
+
+
+def stored_traffic(path):
+    """{kernel: (avg_ns, bytes per dispatch)} from a committed summary, or None
+    when it is missing or was taken on other kernel sources."""
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    if f"source_sha256: {source_digest()}" not in text:
+        return None
+    out = {}
+    block = text.split("Machine-readable", 1)[-1].split("```")[1]
+    for ln in block.strip().splitlines():
+        k, ns, b = ln.split()
+        out[k] = (float(ns), float(b))
+    return out
+
+
+def kernel_of_stage(stage, G):
+    """Kernel symbol (as rocprofv3 shortens it) that a stage launches."""
+    return {"tables": f"k_tables<{G}>", "scan": f"k_scan<{G}>", "collect": f"k_collect<{G}>",
+            "select": f"k_select<{G}>", "attend": f"k_attend<{G},false>",
+            "merge": "k_merge"}[stage]
 
 
 def main():
     args = parse()
+    if args.summarize_profile:
+        summarize_profile(*args.summarize_profile, command=args.profile_command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the PQ-HSA step "
               "shards by sequence or KV head with no exchange, so there is no multi-GPU mode",
@@ -149,9 +290,9 @@ def main():
     if dense_ms is not None:
         log(f"dense split-K step: {dense_ms * 1e3:.2f} µs")
 
-    # per-stage durations (events between launches on the same stream)
+    # per-kernel durations: every kernel launched with its own start/stop events
     nst = pq.NUM_STAGES
-    evs = [[pq.HipEvent() for _ in range(nst + 1)] for _ in range(args.steps)]
+    evs = [[pq.HipEvent() for _ in range(2 * nst)] for _ in range(args.steps)]
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -163,17 +304,17 @@ def main():
     stage_us = np.zeros(nst)
     for i in range(args.steps):
         for s in range(nst):
-            stage_us[s] += evs[i][s].elapsed_ms(evs[i][s + 1]) * 1e3
+            stage_us[s] += evs[i][2 * s].elapsed_ms(evs[i][2 * s + 1]) * 1e3
     stage_us /= args.steps
     dense_stage = None
     if not args.no_dense:
-        devs = [[pq.HipEvent() for _ in range(3)] for _ in range(args.steps)]
+        devs = [[pq.HipEvent() for _ in range(4)] for _ in range(args.steps)]
         for i in range(args.steps):
             L_ = layers[i % n_layers]
             pq.decode_step_profiled(shape, None, q, L_["kc"], L_["vc"], L_["bt"], ctx, out,
                                     dense_ws, devs[i], dense=True)
         torch.cuda.synchronize()
-        dense_stage = [float(np.mean([devs[i][s].elapsed_ms(devs[i][s + 1]) * 1e3
+        dense_stage = [float(np.mean([devs[i][2 * s].elapsed_ms(devs[i][2 * s + 1]) * 1e3
                                       for i in range(args.steps)])) for s in range(2)]
     log("stages µs: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(pq.STAGE_NAMES, stage_us)))
 
@@ -183,7 +324,7 @@ def main():
     n_rows = ws[lay.n_rows:lay.n_rows + BH * 4].view(torch.int32).cpu().numpy()
     k_sel = np.array([min(-(-int(inp.context_lens[b]) * inp.budget_bp // 10000),
                           10 ** 9) for b in range(inp.batch) for _ in range(inp.num_kv_heads)])
-    alg = algorithmic_bytes(inp, n_rows, k_sel)
+    step_bytes, kbytes = algorithmic_bytes(inp, n_rows, k_sel, lay.n_parts)
 
     if args.copy_calibration:
         n = 1 << 28                                   # 1 GiB of fp32
@@ -194,17 +335,22 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: {n * 4} bytes read and written")
 
-    # dominant kernel and its roofline over algorithmic bytes
+    # dominant kernel (longest average duration) and its roofline over its
+    # algorithmic bytes; traffic from the committed counter summary when it was
+    # taken on these kernel sources
     names = pq.STAGE_NAMES
     dom = int(np.argmax(stage_us))
-    per_stage_bytes = {"tables": alg["tables"], "scan": alg["scan"], "collect": None,
-                       "select": None, "attend": alg["exact"] + alg["background"], "merge": None}
-    dom_bytes = per_stage_bytes[names[dom]]
-    achieved = dom_bytes / (stage_us[dom] * 1e-6) / 1e9 if dom_bytes else None
-    roofline = {"bound": "hbm", "kernel": names[dom], "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
-                "traffic": None, "alg_bytes_per_launch": dom_bytes,
-                "launch_us": float(stage_us[dom])}
+    dom_bytes = kbytes[names[dom]]
+    achieved = dom_bytes / (stage_us[dom] * 1e-6) / 1e9
+    prof = stored_traffic(os.path.join(ROOT, "profiles", f"counters_{w['name']}.md"))
+    G = shape.num_q_heads // shape.num_kv_heads
+    kname = kernel_of_stage(names[dom], G)
+    traffic = prof[kname][1] if prof and kname in prof else None
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "kernel": kname, "alg_bytes_per_launch": dom_bytes,
+                "launch_us": float(stage_us[dom]),
+                "traffic_over_alg": (traffic / dom_bytes) if traffic else None}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -239,8 +385,9 @@ def main():
                    "page_size": 16, "layer_copies": n_layers},
         "dense_us": dense_ms * 1e3 if dense_ms else None,
         "speedup_vs_dense": (dense_ms / ms) if dense_ms else None,
-        "step_alg_bytes": alg["total"],
-        "step_alg_gbps": alg["total"] / (ms * 1e-3) / 1e9,
+        "step_alg_bytes": step_bytes,
+        "step_alg_gbps": step_bytes / (ms * 1e-3) / 1e9,
+        "kernel_alg_bytes": kbytes,
         "dense_alg_gbps": (kv_bytes / (dense_ms * 1e-3) / 1e9) if dense_ms else None,
         "stages_us": {n: float(v) for n, v in zip(names, stage_us)},
         "dense_stages_us": ({"splitk": dense_stage[0], "merge": dense_stage[1]}

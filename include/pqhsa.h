@@ -188,11 +188,12 @@ enum {
   PQHSA_NUM_STAGES = 6
 };
 
-/* pqhsa_decode_step that also records stage_events[i] on `stream` right
- * before stage i is launched and stage_events[PQHSA_NUM_STAGES] after the last
- * one (PQHSA_NUM_STAGES + 1 events created by the caller).  With dense != 0
- * it runs pqhsa_dense_decode_step and records events 0 (before the split-K
- * kernel), 1 (before the merge) and 2 (after it). */
+/* pqhsa_decode_step that also times every kernel: stage i is launched with
+ * hipExtLaunchKernel, which stamps stage_events[2i] with the kernel's start
+ * and stage_events[2i+1] with its end (2 * PQHSA_NUM_STAGES events created by
+ * the caller).  With dense != 0 it runs pqhsa_dense_decode_step and times its
+ * two kernels: events 0-1 the split-K kernel, 2-3 the merge.  Results are
+ * identical to the untimed calls. */
 pqhsa_status pqhsa_decode_step_profiled(const pqhsa_shape* shape, const void* index_buf,
                                         const uint16_t* q, const uint16_t* k_cache,
                                         const uint16_t* v_cache, const int32_t* block_table,

@@ -233,11 +233,15 @@ def dense_decode_step(shape: Shape, q, k_cache, v_cache, block_table, context_le
 def decode_step_profiled(shape: Shape, index_buf, q, k_cache, v_cache, block_table,
                          context_lens, out, workspace, events, dense=False, selected=None,
                          lse=None, stream=None):
-    """Like decode_step (or dense_decode_step) but records `events` (HipEvent list)
-    around every stage on the same stream."""
+    """Like decode_step (or dense_decode_step) but times every kernel: `events`
+    is a list of 2 * (number of kernels) HipEvents; events[2i], events[2i+1]
+    take the start and end of kernel i (6 kernels, or 2 with dense=True)."""
     qp, kp, vp, tp, cp, op, lp = _step_ptrs(shape, q, k_cache, v_cache, block_table,
                                             context_lens, out, lse)
     sp = _ptr(selected, "selected", torch.int32, optional=True)
+    need = 2 * (2 if dense else NUM_STAGES)
+    if len(events) < need:
+        raise ValueError(f"decode_step_profiled needs {need} events, got {len(events)}")
     arr = (ctypes.c_void_p * len(events))(*[e.handle for e in events])
     ip = None if dense else _ptr(index_buf, "index_buf", torch.uint8)
     _check("pqhsa_decode_step_profiled", load().pqhsa_decode_step_profiled(

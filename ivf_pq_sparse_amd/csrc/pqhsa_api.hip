@@ -193,9 +193,11 @@ WsPtrs ws_ptrs(const Dims& d, bool dense, void* buf) {
 
 inline pqhsa_status hip_status(hipError_t e) { return e == hipSuccess ? PQHSA_OK : PQHSA_ERR_HIP; }
 
-pqhsa_status record(hipEvent_t* evs, int i, hipStream_t st) {
-  if (!evs) return PQHSA_OK;
-  return hip_status(hipEventRecord(evs[i], st));
+// Launch context of stage i: with an event array, events 2i and 2i+1 take
+// the kernel's start and end.
+Launch stage(hipEvent_t* evs, int i, hipStream_t st) {
+  if (!evs) return Launch{st, nullptr, nullptr};
+  return Launch{st, evs[2 * i], evs[2 * i + 1]};
 }
 
 #define PQHSA_TRY(expr)                         \
@@ -219,11 +221,8 @@ pqhsa_status run_dense(const pqhsa_shape* shape, const uint16_t* q, const uint16
   a.ws = ws_ptrs(d, true, workspace);
   a.q = q; a.kc = k_cache; a.vc = v_cache; a.table = block_table; a.ctx = context_lens;
   a.out = out; a.lse = lse;
-  PQHSA_TRY(record(evs, 0, stream));
-  PQHSA_TRY(hip_status(launch_exact_and_background(a, true, stream)));
-  PQHSA_TRY(record(evs, 1, stream));
-  PQHSA_TRY(hip_status(launch_merge(a, stream)));
-  PQHSA_TRY(record(evs, 2, stream));
+  PQHSA_TRY(hip_status(launch_exact_and_background(a, true, stage(evs, 0, stream))));
+  PQHSA_TRY(hip_status(launch_merge(a, stage(evs, 1, stream))));
   return PQHSA_OK;
 }
 
@@ -245,19 +244,12 @@ pqhsa_status run_step(const pqhsa_shape* shape, const void* index_buf, const uin
   a.ws = ws_ptrs(d, false, workspace);
   a.q = q; a.kc = k_cache; a.vc = v_cache; a.table = block_table; a.ctx = context_lens;
   a.out = out; a.selected = selected; a.max_sel = max_selected(shape); a.lse = lse;
-  PQHSA_TRY(record(evs, PQHSA_STAGE_TABLES, stream));
-  PQHSA_TRY(hip_status(launch_tables(a, stream)));
-  PQHSA_TRY(record(evs, PQHSA_STAGE_SCAN, stream));
-  PQHSA_TRY(hip_status(launch_scan(a, stream)));
-  PQHSA_TRY(record(evs, PQHSA_STAGE_COLLECT, stream));
-  PQHSA_TRY(hip_status(launch_collect(a, stream)));
-  PQHSA_TRY(record(evs, PQHSA_STAGE_SELECT, stream));
-  PQHSA_TRY(hip_status(launch_select(a, stream)));
-  PQHSA_TRY(record(evs, PQHSA_STAGE_ATTEND, stream));
-  PQHSA_TRY(hip_status(launch_exact_and_background(a, false, stream)));
-  PQHSA_TRY(record(evs, PQHSA_STAGE_MERGE, stream));
-  PQHSA_TRY(hip_status(launch_merge(a, stream)));
-  PQHSA_TRY(record(evs, PQHSA_NUM_STAGES, stream));
+  PQHSA_TRY(hip_status(launch_tables(a, stage(evs, PQHSA_STAGE_TABLES, stream))));
+  PQHSA_TRY(hip_status(launch_scan(a, stage(evs, PQHSA_STAGE_SCAN, stream))));
+  PQHSA_TRY(hip_status(launch_collect(a, stage(evs, PQHSA_STAGE_COLLECT, stream))));
+  PQHSA_TRY(hip_status(launch_select(a, stage(evs, PQHSA_STAGE_SELECT, stream))));
+  PQHSA_TRY(hip_status(launch_exact_and_background(a, false, stage(evs, PQHSA_STAGE_ATTEND, stream))));
+  PQHSA_TRY(hip_status(launch_merge(a, stage(evs, PQHSA_STAGE_MERGE, stream))));
   return PQHSA_OK;
 }
 

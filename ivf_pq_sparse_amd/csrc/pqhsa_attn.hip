@@ -356,15 +356,12 @@ __global__ __launch_bounds__(256) void k_merge(StepArgs a) {
 }
 
 template <int G>
-static hipError_t attend_g(const StepArgs& a, bool dense, hipStream_t st) {
+static hipError_t attend_g(const StepArgs& a, bool dense, const Launch& l) {
   const int BH = a.d.B * a.d.Hkv;
-  if (dense) {
-    hipLaunchKernelGGL((k_attend<G, true>), dim3(BH * a.d.n_exact_splits), dim3(256), 0, st, a);
-  } else {
-    hipLaunchKernelGGL((k_attend<G, false>),
-                       dim3(BH * (a.d.n_exact_splits + a.d.n_bg_splits)), dim3(256), 0, st, a);
-  }
-  return hipGetLastError();
+  if (dense)
+    return launch_kernel(k_attend<G, true>, dim3(BH * a.d.n_exact_splits), dim3(256), 0, l, a);
+  return launch_kernel(k_attend<G, false>, dim3(BH * (a.d.n_exact_splits + a.d.n_bg_splits)),
+                       dim3(256), 0, l, a);
 }
 
 #define PQHSA_G_DISPATCH2(fn, ...)                  \
@@ -376,17 +373,16 @@ static hipError_t attend_g(const StepArgs& a, bool dense, hipStream_t st) {
   }                                                 \
   return hipErrorInvalidValue;
 
-hipError_t launch_exact_and_background(const StepArgs& a, bool dense, hipStream_t st) {
-  PQHSA_G_DISPATCH2(attend_g, a, dense, st)
+hipError_t launch_exact_and_background(const StepArgs& a, bool dense, const Launch& l) {
+  PQHSA_G_DISPATCH2(attend_g, a, dense, l)
 }
 
-hipError_t launch_merge(const StepArgs& a, hipStream_t st) {
+hipError_t launch_merge(const StepArgs& a, const Launch& l) {
   const size_t lds = ((size_t)2 * a.d.n_parts + kD) * sizeof(float);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_merge),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_merge, dim3(a.d.B * a.d.Hq), dim3(256), lds, st, a);
-  return hipGetLastError();
+  return launch_kernel(k_merge, dim3(a.d.B * a.d.Hq), dim3(256), lds, l, a);
 }
 
 }  // namespace pqhsa

@@ -2,6 +2,7 @@
 // kernel launchers shared by the translation units.  Not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -229,12 +230,31 @@ __device__ __forceinline__ void entry_logits(const float* __restrict__ lut, cons
 }
 
 // ---------------------------------------------------------------- launchers
+// Stream and optional timing events of one kernel launch.  With events the
+// launch goes through hipExtLaunchKernel, which stamps the two events with the
+// kernel's own start and end (no gap to a separately recorded marker).
+struct Launch {
+  hipStream_t st;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+template <typename A>
+inline hipError_t launch_kernel(void (*kernel)(A), dim3 grid, dim3 block, size_t lds,
+                                const Launch& l, A arg) {
+  void* argv[1] = {&arg};
+  if (l.start)
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds, l.st,
+                              l.start, l.stop, 0);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds, l.st);
+}
+
 hipError_t launch_upload(const UploadArgs& a, hipStream_t st);
-hipError_t launch_tables(const StepArgs& a, hipStream_t st);
-hipError_t launch_scan(const StepArgs& a, hipStream_t st);
-hipError_t launch_collect(const StepArgs& a, hipStream_t st);
-hipError_t launch_select(const StepArgs& a, hipStream_t st);
-hipError_t launch_exact_and_background(const StepArgs& a, bool dense, hipStream_t st);
-hipError_t launch_merge(const StepArgs& a, hipStream_t st);
+hipError_t launch_tables(const StepArgs& a, const Launch& l);
+hipError_t launch_scan(const StepArgs& a, const Launch& l);
+hipError_t launch_collect(const StepArgs& a, const Launch& l);
+hipError_t launch_select(const StepArgs& a, const Launch& l);
+hipError_t launch_exact_and_background(const StepArgs& a, bool dense, const Launch& l);
+hipError_t launch_merge(const StepArgs& a, const Launch& l);
 
 }  // namespace pqhsa

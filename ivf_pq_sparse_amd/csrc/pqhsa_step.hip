@@ -143,8 +143,8 @@ struct ScanRound {
 
 template <int G>
 __global__ __launch_bounds__(kScanThreads) void k_scan(StepArgs a) {
-  // tiles in flight per wave; fewer at G = 8 to stay within 128 VGPRs
-  constexpr int P = G == 8 ? 2 : 4;
+  // tiles in flight per wave; fewer at G >= 4 to stay within 128 VGPRs
+  constexpr int P = G >= 4 ? 2 : 4;
   extern __shared__ float4 smem4[];
   float* lut = reinterpret_cast<float*>(smem4);
   uint32_t* hist = reinterpret_cast<uint32_t*>(lut + kM * kKsub * G);
@@ -827,37 +827,36 @@ __global__ __launch_bounds__(kCollectThreads) void k_collect(StepArgs a) {
   return hipErrorInvalidValue;
 
 template <int G>
-static hipError_t tables_g(const StepArgs& a, hipStream_t st) {
+static hipError_t tables_g(const StepArgs& a, const Launch& l) {
   const int BH = a.d.B * a.d.Hkv;
-  hipLaunchKernelGGL(k_tables<G>, dim3(BH, kM + (a.d.L + 15) / 16), dim3(256), 0, st, a);
-  return hipGetLastError();
+  return launch_kernel(k_tables<G>, dim3(BH, kM + (a.d.L + 15) / 16), dim3(256), 0, l, a);
 }
-hipError_t launch_tables(const StepArgs& a, hipStream_t st) { PQHSA_G_DISPATCH(tables_g, a, st) }
+hipError_t launch_tables(const StepArgs& a, const Launch& l) { PQHSA_G_DISPATCH(tables_g, a, l) }
 
 template <int G>
-static hipError_t scan_g(const StepArgs& a, hipStream_t st) {
+static hipError_t scan_g(const StepArgs& a, const Launch& l) {
   const int BH = a.d.B * a.d.Hkv;
   const size_t lds = (size_t)kM * kKsub * G * sizeof(float) + kHistBins * sizeof(uint32_t);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_scan<G>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_scan<G>, dim3(BH * a.d.scan_blocks), dim3(kScanThreads), lds, st, a);
-  return hipGetLastError();
+  return launch_kernel(k_scan<G>, dim3(BH * a.d.scan_blocks), dim3(kScanThreads), lds, l, a);
 }
-hipError_t launch_scan(const StepArgs& a, hipStream_t st) { PQHSA_G_DISPATCH(scan_g, a, st) }
+hipError_t launch_scan(const StepArgs& a, const Launch& l) { PQHSA_G_DISPATCH(scan_g, a, l) }
 
 template <int G>
-static hipError_t collect_g(const StepArgs& a, hipStream_t st) {
+static hipError_t collect_g(const StepArgs& a, const Launch& l) {
   const int BH = a.d.B * a.d.Hkv;
   const size_t lds = (size_t)kCollectEntries * (sizeof(int) + sizeof(uint2));
-  hipLaunchKernelGGL(k_collect<G>, dim3(BH * a.d.collect_slices), dim3(kCollectThreads), lds,
-                     st, a);
-  return hipGetLastError();
+  return launch_kernel(k_collect<G>, dim3(BH * a.d.collect_slices), dim3(kCollectThreads), lds,
+                       l, a);
 }
-hipError_t launch_collect(const StepArgs& a, hipStream_t st) { PQHSA_G_DISPATCH(collect_g, a, st) }
+hipError_t launch_collect(const StepArgs& a, const Launch& l) {
+  PQHSA_G_DISPATCH(collect_g, a, l)
+}
 
 template <int G>
-static hipError_t select_g(const StepArgs& a, hipStream_t st) {
+static hipError_t select_g(const StepArgs& a, const Launch& l) {
   const int BH = a.d.B * a.d.Hkv;
   const size_t wsel = (size_t)a.d.L * G * sizeof(unsigned long long);
   const size_t lds = ((size_t)a.d.nwords * 4 + 15) / 16 * 16 + kWinCap * sizeof(uint2) +
@@ -865,9 +864,8 @@ static hipError_t select_g(const StepArgs& a, hipStream_t st) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_select<G>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_select<G>, dim3(BH), dim3(kSelectThreads), lds, st, a);
-  return hipGetLastError();
+  return launch_kernel(k_select<G>, dim3(BH), dim3(kSelectThreads), lds, l, a);
 }
-hipError_t launch_select(const StepArgs& a, hipStream_t st) { PQHSA_G_DISPATCH(select_g, a, st) }
+hipError_t launch_select(const StepArgs& a, const Launch& l) { PQHSA_G_DISPATCH(select_g, a, l) }
 
 }  // namespace pqhsa

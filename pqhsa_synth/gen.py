@@ -27,6 +27,8 @@ of them are handed to the index, the rest form the unindexed tail.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -153,12 +155,14 @@ def make_step_inputs(workload: int | dict, *, workload_id: int | None = None,
                      context_lens=None, n_tail=None, n_planted=None, noise: float = 0.02,
                      dyadic: bool = False, constant_v: float | None = None,
                      planted_strength: float = 3.0, one_token_per_list: bool = False,
-                     **overrides) -> StepInputs:
+                     workers: int | None = None, **overrides) -> StepInputs:
     """Build one decode step's inputs from a workload (an id in WORKLOADS or a dict).
 
     Any workload field may be overridden by keyword (num_lists, budget_bp, ...).
     context_lens may give a per-sequence length; n_tail is the unindexed tail
-    length of every sequence (clamped to its length).
+    length of every sequence (clamped to its length).  Large inputs are drawn
+    by up to `workers` threads (default: the CPU count, at most 16); the
+    result does not depend on the thread count.
     """
     if isinstance(workload, int):
         wid = workload if workload_id is None else workload_id
@@ -185,14 +189,27 @@ def make_step_inputs(workload: int | dict, *, workload_id: int | None = None,
     lists = np.zeros((B, Hkv, Tmax), np.int32)
     codes = np.zeros((B, Hkv, Tmax, PQ_M), np.uint8)
     planted_all = []
+
+    def fill(bh):
+        # every (b, h) has its own generator, so the draws do not depend on
+        # the order in which worker threads run
+        b, h = divmod(bh, Hkv)
+        T = int(context_lens[b])
+        d = draw_head(wid, b, h, T, L, noise=noise, dyadic=dyadic, constant_v=constant_v,
+                      one_token_per_list=one_token_per_list)
+        cents[b, h], books[b, h] = d.centroids, d.codebooks
+        lists[b, h, :T], codes[b, h, :T] = d.list_ids, d.codes
+        k_bits[b, h, :T], v_bits[b, h, :T] = d.k_bits, d.v_bits
+
+    n_workers = max(1, min(workers or os.cpu_count() or 1, 16, B * Hkv))
+    if n_workers == 1 or int(context_lens.sum()) * Hkv < (1 << 20):
+        for bh in range(B * Hkv):
+            fill(bh)
+    else:
+        with ThreadPoolExecutor(n_workers) as ex:
+            list(ex.map(fill, range(B * Hkv)))
     for b in range(B):
         T = int(context_lens[b])
-        for h in range(Hkv):
-            d = draw_head(wid, b, h, T, L, noise=noise, dyadic=dyadic, constant_v=constant_v,
-                          one_token_per_list=one_token_per_list)
-            cents[b, h], books[b, h] = d.centroids, d.codebooks
-            lists[b, h, :T], codes[b, h, :T] = d.list_ids, d.codes
-            k_bits[b, h, :T], v_bits[b, h, :T] = d.k_bits, d.v_bits
         rng = np.random.default_rng([wid, b])
         lo = min(w["n_sink"], T)
         hi = max(T - max(w["n_recent"], T - int(n_indexed[b])), lo)

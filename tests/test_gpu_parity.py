@@ -51,6 +51,23 @@ def test_llama_32k_parity():
     parity(make_step_inputs(1), what="workload 1 (32K, 32q/8kv, L256)")
 
 
+# Full-size workloads in the launch configuration bench.py times (same shape
+# fields, so the same grids): every head at 128K and 512K, sampled heads of
+# the 16-sequence batch, each head checked against the oracle in full.
+def test_llama_128k_parity():
+    parity(make_step_inputs(2), what="workload 2 (128K, 32q/8kv, L512, k=1311)")
+
+
+def test_llama_128k_batch16_parity_sampled_heads():
+    heads = [(0, 0), (3, 5), (7, 2), (10, 7), (15, 1), (15, 6)]
+    parity(make_step_inputs(3), heads=heads,
+           what="workload 3 (16 x 128K, 32q/8kv, L512), 6 sampled (seq, KV head)")
+
+
+def test_qwen_512k_parity():
+    parity(make_step_inputs(4), what="workload 4 (512K, 32q/4kv G=8, L1024, k=5243)")
+
+
 def test_full_budget_is_dense_on_gpu():
     import oracle
     inp = make_step_inputs(1, context_lens=[4100], budget_bp=10000, num_lists=32, workload_id=9)
