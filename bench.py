@@ -73,6 +73,10 @@ def algorithmic_bytes(inp, n_rows_per_head, k_sel, n_parts):
       attend:  512 B K+V + 4 B row id per exact row; per head the means
                (L*512 B), bins and selected weights; writes the partials
       merge:   reads the partials (132*4 B each), writes O (512 B per q head)
+      fused:   the whole step in one kernel: 16 B codes + 4 B position per
+               indexed entry, 512 B K+V + 4 B page-table entry per exact row,
+               per head the codebooks, centroids and means, q and O (its
+               scratch stays in L2 and is not counted)
     """
     B, Hkv, Hq = inp.batch, inp.num_kv_heads, inp.num_q_heads
     G, L = Hq // Hkv, inp.num_lists
@@ -84,6 +88,8 @@ def algorithmic_bytes(inp, n_rows_per_head, k_sel, n_parts):
     partials = B * Hq * n_parts * 132 * 4
     rec = 8 + 4 * G
     k = {
+        "fused": (n_idx * (16 + 4) + rows * (512 + 4) + BH * (16 * 256 * 8 * 4 + 2 * L * 512)
+                  + B * Hq * (256 + 512)),
         "tables": B * Hq * 256 + BH * (16 * 256 * 8 * 4 + L * 512 + lut + qc),
         "scan": n_idx * (16 + 4 + 4) + BH * (lut + qc + bins + (L + 1) * 4),
         "collect": n_idx * 4 + BH * 4096 * 4 + ksum * rec,
@@ -203,7 +209,8 @@ def stored_traffic(path):
 
 def kernel_of_stage(stage, G):
     """Kernel symbol (as rocprofv3 shortens it) that a stage launches."""
-    return {"tables": f"k_tables<{G}>", "scan": f"k_scan<{G}>", "collect": f"k_collect<{G}>",
+    return {"fused": f"k_fused<{G}>",
+            "tables": f"k_tables<{G}>", "scan": f"k_scan<{G}>", "collect": f"k_collect<{G}>",
             "select": f"k_select<{G}>", "attend": f"k_attend<{G},false>",
             "merge": "k_merge"}[stage]
 
@@ -290,33 +297,35 @@ def main():
     if dense_ms is not None:
         log(f"dense split-K step: {dense_ms * 1e3:.2f} µs")
 
-    # per-kernel durations: every kernel launched with its own start/stop events
-    nst = pq.NUM_STAGES
-    evs = [[pq.HipEvent() for _ in range(2 * nst)] for _ in range(args.steps)]
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        L_ = layers[i % n_layers]
-        pq.decode_step_profiled(shape, L_["dec"].index, q, L_["kc"], L_["vc"], L_["bt"], ctx, out,
-                                ws, evs[i])
-    torch.cuda.synchronize()
-    stage_us = np.zeros(nst)
-    for i in range(args.steps):
-        for s in range(nst):
-            stage_us[s] += evs[i][2 * s].elapsed_ms(evs[i][2 * s + 1]) * 1e3
-    stage_us /= args.steps
-    dense_stage = None
-    if not args.no_dense:
-        devs = [[pq.HipEvent() for _ in range(4)] for _ in range(args.steps)]
+    # per-kernel durations: the same steps through the profiled entry point,
+    # every kernel with its own start/stop events on the step's stream
+    def kernel_us(variant):
+        wsv = dense_ws if variant == pq.VARIANT_DENSE else ws
+        evs = [[pq.HipEvent() for _ in range(2 * pq.NUM_STAGES)] for _ in range(args.steps)]
+        for i in range(args.warmup):
+            step(i, variant == pq.VARIANT_DENSE)
+        torch.cuda.synchronize()
+        nk = 0
         for i in range(args.steps):
             L_ = layers[i % n_layers]
-            pq.decode_step_profiled(shape, None, q, L_["kc"], L_["vc"], L_["bt"], ctx, out,
-                                    dense_ws, devs[i], dense=True)
+            nk = pq.decode_step_profiled(shape, L_["dec"].index, q, L_["kc"], L_["vc"], L_["bt"],
+                                         ctx, out, wsv, evs[i], variant=variant)
         torch.cuda.synchronize()
-        dense_stage = [float(np.mean([devs[i][2 * s].elapsed_ms(devs[i][2 * s + 1]) * 1e3
-                                      for i in range(args.steps)])) for s in range(2)]
-    log("stages µs: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(pq.STAGE_NAMES, stage_us)))
+        t = np.array([[evs[i][2 * k].elapsed_ms(evs[i][2 * k + 1]) * 1e3 for k in range(nk)]
+                      for i in range(args.steps)])
+        return t.mean(axis=0)
+
+    step_k = kernel_us(pq.VARIANT_DEFAULT)
+    fused = len(step_k) == 1
+    names = ["fused"] if fused else list(pq.STAGE_NAMES)
+    stage_us = step_k
+    staged_us = kernel_us(pq.VARIANT_STAGED)
+    dense_stage = None if args.no_dense else kernel_us(pq.VARIANT_DENSE)
+    log("step kernels µs: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(names, stage_us)))
+    log("staged kernels µs: " + ", ".join(f"{n}={v:.2f}" for n, v in zip(pq.STAGE_NAMES,
+                                                                          staged_us)))
+    if fused and pq.PQHSADecoder.flags(layers[0]["dec"]) != 0:
+        raise SystemExit("a barrier wait of the fused step timed out")
 
     # exact rows and k per head from the last step's workspace
     lay = pq.workspace_layout(shape)
@@ -338,7 +347,6 @@ def main():
     # dominant kernel (longest average duration) and its roofline over its
     # algorithmic bytes; traffic from the committed counter summary when it was
     # taken on these kernel sources
-    names = pq.STAGE_NAMES
     dom = int(np.argmax(stage_us))
     dom_bytes = kbytes[names[dom]]
     achieved = dom_bytes / (stage_us[dom] * 1e-6) / 1e9
@@ -389,9 +397,10 @@ def main():
         "step_alg_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "kernel_alg_bytes": kbytes,
         "dense_alg_gbps": (kv_bytes / (dense_ms * 1e-3) / 1e9) if dense_ms else None,
-        "stages_us": {n: float(v) for n, v in zip(names, stage_us)},
-        "dense_stages_us": ({"splitk": dense_stage[0], "merge": dense_stage[1]}
-                            if dense_stage else None),
+        "kernels_us": {n: float(v) for n, v in zip(names, stage_us)},
+        "staged_kernels_us": {n: float(v) for n, v in zip(pq.STAGE_NAMES, staged_us)},
+        "dense_kernels_us": ({"splitk": float(dense_stage[0]), "merge": float(dense_stage[1])}
+                             if dense_stage is not None else None),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

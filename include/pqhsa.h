@@ -84,7 +84,10 @@ size_t pqhsa_index_bytes(const pqhsa_shape* shape);
 size_t pqhsa_upload_workspace_bytes(const pqhsa_shape* shape);
 
 /* Bytes of scratch workspace for one decode step; dense != 0 sizes it for
- * pqhsa_dense_decode_step instead.  0 if the shape is invalid. */
+ * pqhsa_dense_decode_step instead.  0 if the shape is invalid.  A decode-step
+ * workspace must be zero-filled before its first use (it holds per-head
+ * counters and a histogram that every step leaves cleared for the next one);
+ * it needs no further clearing while it is used for one shape. */
 size_t pqhsa_workspace_bytes(const pqhsa_shape* shape, int dense);
 
 /* Capacity of the optional `selected` output per (sequence, KV head):
@@ -154,6 +157,15 @@ pqhsa_status pqhsa_index_dropped(const pqhsa_shape* shape, const void* index_buf
  * over the group's query heads, the overlap of the recent window with the
  * tail, and the tie rule are readings where the page is silent.)
  */
+/* Execution: when its grid fits the device at one block per CU, the step
+ * runs as one kernel whose blocks of a KV head share that head's clusters and
+ * meet at two barriers (fused step); otherwise as the six kernels listed
+ * below (staged step).  Both compute the same quantities.  The fused step
+ * assumes its blocks can all be resident together: on a device whose CUs are
+ * partly withheld (CU masking, long-running concurrent kernels) a barrier wait
+ * may time out after about 2 s, which sets bit 0 of the workspace flags
+ * (pqhsa_workspace_layout) and leaves that step's results invalid; the staged
+ * variant of pqhsa_decode_step_profiled has no such requirement. */
 pqhsa_status pqhsa_decode_step(const pqhsa_shape* shape, const void* index_buf,
                                const uint16_t* q, const uint16_t* k_cache,
                                const uint16_t* v_cache, const int32_t* block_table,
@@ -177,7 +189,7 @@ pqhsa_status pqhsa_dense_decode_step(const pqhsa_shape* shape, const uint16_t* q
                                      float* out, float* lse, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream);
 
-/* Kernels of pqhsa_decode_step, in launch order, for profiling. */
+/* Kernels of the staged decode step, in launch order, for profiling. */
 enum {
   PQHSA_STAGE_TABLES = 0,     /* per-query lookup tables */
   PQHSA_STAGE_SCAN = 1,       /* code scan: approximate logits, keys, cluster bins */
@@ -188,19 +200,27 @@ enum {
   PQHSA_NUM_STAGES = 6
 };
 
-/* pqhsa_decode_step that also times every kernel: stage i is launched with
- * hipExtLaunchKernel, which stamps stage_events[2i] with the kernel's start
- * and stage_events[2i+1] with its end (2 * PQHSA_NUM_STAGES events created by
- * the caller).  With dense != 0 it runs pqhsa_dense_decode_step and times its
- * two kernels: events 0-1 the split-K kernel, 2-3 the merge.  Results are
- * identical to the untimed calls. */
+/* Variants of pqhsa_decode_step_profiled. */
+enum {
+  PQHSA_VARIANT_DEFAULT = 0,  /* exactly what pqhsa_decode_step runs */
+  PQHSA_VARIANT_STAGED = 1,   /* the six staged kernels, whatever the shape */
+  PQHSA_VARIANT_DENSE = 2     /* pqhsa_dense_decode_step (index_buf unused) */
+};
+
+/* A decode step that also times its kernels.  events holds 2 * PQHSA_NUM_STAGES
+ * events created by the caller; kernel i of the step gets events[2i] (start)
+ * and events[2i+1] (end), and *n_kernels (if not NULL) is set to the number
+ * of kernels launched.  Kernels are launched with hipExtLaunchKernel, whose
+ * events stamp each kernel's own start and end.  Results are those of the
+ * untimed call of the same variant. */
 pqhsa_status pqhsa_decode_step_profiled(const pqhsa_shape* shape, const void* index_buf,
                                         const uint16_t* q, const uint16_t* k_cache,
                                         const uint16_t* v_cache, const int32_t* block_table,
                                         const int32_t* context_lens, float* out,
                                         int32_t* selected, float* lse, void* workspace,
-                                        size_t workspace_bytes, int dense,
-                                        hipEvent_t* stage_events, hipStream_t stream);
+                                        size_t workspace_bytes, int variant,
+                                        hipEvent_t* events, int32_t* n_kernels,
+                                        hipStream_t stream);
 
 /* Byte offsets of the intermediate arrays inside the decode workspace, so
  * tests can check each stage.  Layouts (bh = b * Hkv + h):
@@ -212,9 +232,14 @@ pqhsa_status pqhsa_decode_step_profiled(const pqhsa_shape* shape, const void* in
  *           the candidates' base-2 logits relative to that max
  *   rows    int32 [B*Hkv][max_context] exact rows: sink, selected, recent/tail
  *   n_rows  int32 [B*Hkv]
- *   partials float [B][Hq][n_parts][132]: (m in base 2, l, pad, pad, acc[128]) */
+ *   partials float [B][Hq][n_parts][132]: (m in base 2, l, pad, pad, acc[128])
+ *   flags   uint32: bit 0 set if a barrier wait of the fused step ever timed
+ *           out (its results are then not valid)
+ * The staged step fills lut, qc, keys, bins, rows, n_rows and partials; the
+ * fused step fills qc and bins of every cluster, keys, n_rows, and rows in a
+ * per-block order. */
 typedef struct pqhsa_ws_layout {
-  size_t lut, qc, keys, bins, rows, n_rows, partials;
+  size_t lut, qc, keys, bins, rows, n_rows, partials, flags;
   int32_t n_exact_splits, n_bg_splits, n_parts;
 } pqhsa_ws_layout;
 pqhsa_status pqhsa_workspace_layout(const pqhsa_shape* shape, int dense, pqhsa_ws_layout* out);

@@ -13,6 +13,9 @@ from . import _lib
 from ._lib import (  # noqa: F401
     EXPORTS,
     NUM_STAGES,
+    VARIANT_DEFAULT,
+    VARIANT_DENSE,
+    VARIANT_STAGED,
     STAGE_NAMES,
     HipEvent,
     PQHSAError,
@@ -49,9 +52,12 @@ class PQHSADecoder:
         if nb == 0:
             raise PQHSAError("pqhsa_index_bytes", 1)
         self.index = torch.empty(nb, dtype=torch.uint8, device=self.device)
-        self.workspace = torch.empty(workspace_bytes(shape, False), dtype=torch.uint8,
+        # zero-filled once: the step keeps per-head counters here and leaves
+        # them cleared for the next step
+        self.workspace = torch.zeros(workspace_bytes(shape, False), dtype=torch.uint8,
                                      device=self.device)
         self._dense_ws = None
+        self._events = None
         self.max_selected = max_selected(shape)
 
     def upload(self, centroids, codebooks, list_ids, codes, n_indexed, v_cache, block_table,
@@ -63,7 +69,9 @@ class PQHSADecoder:
         self._upload_ws = ws          # keep alive until the stream has used it
 
     def step(self, q, k_cache, v_cache, block_table, context_lens, out=None, selected=False,
-             lse=False, stream=None):
+             lse=False, stream=None, staged=False):
+        """One decode step.  staged=True runs the six staged kernels instead
+        of whatever pqhsa_decode_step would choose (for cross-checks)."""
         s = self.shape
         if out is None:
             out = torch.empty(s.batch, s.num_q_heads, 128, dtype=torch.float32, device=self.device)
@@ -71,9 +79,22 @@ class PQHSADecoder:
         sel = (torch.full((s.batch, s.num_kv_heads, max(self.max_selected, 1)), -1,
                           dtype=torch.int32, device=self.device) if selected else None)
         ls = torch.empty(s.batch, s.num_q_heads, dtype=torch.float32, device=self.device) if lse else None
-        decode_step(s, self.index, q, k_cache, v_cache, block_table, context_lens, out,
-                    self.workspace, selected=sel, lse=ls, stream=stream)
+        if staged:
+            if self._events is None:
+                self._events = [HipEvent() for _ in range(2 * NUM_STAGES)]
+            decode_step_profiled(s, self.index, q, k_cache, v_cache, block_table, context_lens,
+                                 out, self.workspace, self._events, variant=VARIANT_STAGED,
+                                 selected=sel, lse=ls, stream=stream)
+        else:
+            decode_step(s, self.index, q, k_cache, v_cache, block_table, context_lens, out,
+                        self.workspace, selected=sel, lse=ls, stream=stream)
         return out, sel, ls
+
+    def flags(self) -> int:
+        """The workspace's status word (bit 0: a fused-step barrier wait timed
+        out).  Synchronises with the device through the copy."""
+        off = workspace_layout(self.shape).flags
+        return int(self.workspace[off:off + 4].view(torch.int32).item())
 
     def dense_workspace(self):
         if self._dense_ws is None:

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libpqhsa.so")
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "buffer too small",
           4: "HIP error"}
 NUM_STAGES = 6
+VARIANT_DEFAULT, VARIANT_STAGED, VARIANT_DENSE = 0, 1, 2
 STAGE_NAMES = ["tables", "scan", "collect", "select", "attend", "merge"]
 
 
@@ -40,7 +41,7 @@ class Shape(ctypes.Structure):
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
-        "lut", "qc", "keys", "bins", "rows", "n_rows", "partials")] + [
+        "lut", "qc", "keys", "bins", "rows", "n_rows", "partials", "flags")] + [
         (n, ctypes.c_int32) for n in ("n_exact_splits", "n_bg_splits", "n_parts")]
 
 
@@ -80,7 +81,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "pqhsa_decode_step": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "pqhsa_dense_decode_step": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, SZ, P]),
         "pqhsa_decode_step_profiled": (ctypes.c_int,
-                                       [S, P, P, P, P, P, P, P, P, P, P, SZ, ctypes.c_int, P, P]),
+                                       [S, P, P, P, P, P, P, P, P, P, P, SZ, ctypes.c_int, P,
+                                        ctypes.POINTER(ctypes.c_int32), P]),
         "pqhsa_workspace_layout": (ctypes.c_int, [S, ctypes.c_int, ctypes.POINTER(WsLayout)]),
         "pqhsa_index_layout_of": (ctypes.c_int, [S, ctypes.POINTER(IndexLayout)]),
         "pqhsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -231,23 +233,26 @@ def dense_decode_step(shape: Shape, q, k_cache, v_cache, block_table, context_le
 
 
 def decode_step_profiled(shape: Shape, index_buf, q, k_cache, v_cache, block_table,
-                         context_lens, out, workspace, events, dense=False, selected=None,
-                         lse=None, stream=None):
-    """Like decode_step (or dense_decode_step) but times every kernel: `events`
-    is a list of 2 * (number of kernels) HipEvents; events[2i], events[2i+1]
-    take the start and end of kernel i (6 kernels, or 2 with dense=True)."""
+                         context_lens, out, workspace, events, variant=VARIANT_DEFAULT,
+                         selected=None, lse=None, stream=None) -> int:
+    """A decode step (variant: VARIANT_DEFAULT, VARIANT_STAGED or VARIANT_DENSE)
+    that times its kernels: events[2i], events[2i+1] take the start and end of
+    kernel i.  `events` holds 2 * NUM_STAGES HipEvents.  Returns the number of
+    kernels launched."""
     qp, kp, vp, tp, cp, op, lp = _step_ptrs(shape, q, k_cache, v_cache, block_table,
                                             context_lens, out, lse)
     sp = _ptr(selected, "selected", torch.int32, optional=True)
-    need = 2 * (2 if dense else NUM_STAGES)
-    if len(events) < need:
-        raise ValueError(f"decode_step_profiled needs {need} events, got {len(events)}")
+    if len(events) < 2 * NUM_STAGES:
+        raise ValueError(f"decode_step_profiled needs {2 * NUM_STAGES} events, got {len(events)}")
     arr = (ctypes.c_void_p * len(events))(*[e.handle for e in events])
+    dense = variant == VARIANT_DENSE
     ip = None if dense else _ptr(index_buf, "index_buf", torch.uint8)
+    nk = ctypes.c_int32(0)
     _check("pqhsa_decode_step_profiled", load().pqhsa_decode_step_profiled(
         ctypes.byref(shape), ip, qp, kp, vp, tp, cp, op, sp, lp,
-        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), int(bool(dense)), arr,
-        _stream(stream)))
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), int(variant), arr,
+        ctypes.byref(nk), _stream(stream)))
+    return nk.value
 
 
 # ------------------------------------------------------------------ HIP events

@@ -119,7 +119,7 @@ IndexLayout index_layout(const Dims& d) {
 
 struct WsLayout {
   size_t lut, qc, keys, bins, hist, seg_above, seg_aw, seg_tie, seg_w, seg_cnt, wsel, rows, n_rows,
-      partials, total;
+      fsync, fflags, fcnt, fpart, partials, total;
 };
 
 WsLayout ws_layout(const Dims& d, bool dense) {
@@ -141,6 +141,10 @@ WsLayout ws_layout(const Dims& d, bool dense) {
     l.wsel = o;       o = align_up(o + BH * d.L * d.G * sizeof(unsigned long long));
     l.rows = o;       o = align_up(o + BH * d.cap * sizeof(int32_t));
     l.n_rows = o;     o = align_up(o + BH * sizeof(int32_t));
+    l.fsync = o;      o = align_up(o + BH * 4 * sizeof(uint32_t));
+    l.fflags = o;     o = align_up(o + sizeof(uint32_t));
+    l.fcnt = o;       o = align_up(o + BH * kMaxFusedP * sizeof(unsigned long long));
+    l.fpart = o;      o = align_up(o + BH * d.G * kMaxFusedP * kPart * sizeof(float));
   }
   l.partials = o;     o = align_up(o + (size_t)d.B * d.Hq * d.n_parts * kPart * sizeof(float));
   l.total = o;
@@ -186,6 +190,10 @@ WsPtrs ws_ptrs(const Dims& d, bool dense, void* buf) {
     w.wsel = reinterpret_cast<unsigned long long*>(p + l.wsel);
     w.rows = reinterpret_cast<int32_t*>(p + l.rows);
     w.n_rows = reinterpret_cast<int32_t*>(p + l.n_rows);
+    w.fsync = reinterpret_cast<uint32_t*>(p + l.fsync);
+    w.fflags = reinterpret_cast<uint32_t*>(p + l.fflags);
+    w.fcnt = reinterpret_cast<unsigned long long*>(p + l.fcnt);
+    w.fpart = reinterpret_cast<float*>(p + l.fpart);
   }
   w.partials = reinterpret_cast<float*>(p + l.partials);
   return w;
@@ -209,7 +217,7 @@ Launch stage(hipEvent_t* evs, int i, hipStream_t st) {
 pqhsa_status run_dense(const pqhsa_shape* shape, const uint16_t* q, const uint16_t* k_cache,
                        const uint16_t* v_cache, const int32_t* block_table,
                        const int32_t* context_lens, float* out, float* lse, void* workspace,
-                       size_t ws_bytes, hipEvent_t* evs, hipStream_t stream) {
+                       size_t ws_bytes, hipEvent_t* evs, int* n_kernels, hipStream_t stream) {
   PQHSA_TRY(validate(shape, true));
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out || !workspace)
     return PQHSA_ERR_INVALID_ARG;
@@ -223,6 +231,7 @@ pqhsa_status run_dense(const pqhsa_shape* shape, const uint16_t* q, const uint16
   a.out = out; a.lse = lse;
   PQHSA_TRY(hip_status(launch_exact_and_background(a, true, stage(evs, 0, stream))));
   PQHSA_TRY(hip_status(launch_merge(a, stage(evs, 1, stream))));
+  if (n_kernels) *n_kernels = 2;
   return PQHSA_OK;
 }
 
@@ -230,7 +239,7 @@ pqhsa_status run_step(const pqhsa_shape* shape, const void* index_buf, const uin
                       const uint16_t* k_cache, const uint16_t* v_cache,
                       const int32_t* block_table, const int32_t* context_lens, float* out,
                       int32_t* selected, float* lse, void* workspace, size_t ws_bytes,
-                      hipEvent_t* evs, hipStream_t stream) {
+                      bool staged, hipEvent_t* evs, int* n_kernels, hipStream_t stream) {
   PQHSA_TRY(validate(shape, false));
   if (!index_buf || !q || !k_cache || !v_cache || !block_table || !context_lens || !out ||
       !workspace)
@@ -244,12 +253,22 @@ pqhsa_status run_step(const pqhsa_shape* shape, const void* index_buf, const uin
   a.ws = ws_ptrs(d, false, workspace);
   a.q = q; a.kc = k_cache; a.vc = v_cache; a.table = block_table; a.ctx = context_lens;
   a.out = out; a.selected = selected; a.max_sel = max_selected(shape); a.lse = lse;
+  const int fP = staged ? 0 : fused_blocks_per_head(d);
+  if (fP > 0) {
+    // the whole step in one kernel
+    a.d.fP = fP;
+    a.d.fcpb = ceil_div(d.L, fP);
+    PQHSA_TRY(hip_status(launch_fused(a, stage(evs, 0, stream))));
+    if (n_kernels) *n_kernels = 1;
+    return PQHSA_OK;
+  }
   PQHSA_TRY(hip_status(launch_tables(a, stage(evs, PQHSA_STAGE_TABLES, stream))));
   PQHSA_TRY(hip_status(launch_scan(a, stage(evs, PQHSA_STAGE_SCAN, stream))));
   PQHSA_TRY(hip_status(launch_collect(a, stage(evs, PQHSA_STAGE_COLLECT, stream))));
   PQHSA_TRY(hip_status(launch_select(a, stage(evs, PQHSA_STAGE_SELECT, stream))));
   PQHSA_TRY(hip_status(launch_exact_and_background(a, false, stage(evs, PQHSA_STAGE_ATTEND, stream))));
   PQHSA_TRY(hip_status(launch_merge(a, stage(evs, PQHSA_STAGE_MERGE, stream))));
+  if (n_kernels) *n_kernels = PQHSA_NUM_STAGES;
   return PQHSA_OK;
 }
 
@@ -333,7 +352,7 @@ pqhsa_status pqhsa_decode_step(const pqhsa_shape* shape, const void* index_buf,
                                float* lse, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
   return run_step(shape, index_buf, q, k_cache, v_cache, block_table, context_lens, out,
-                  selected, lse, workspace, workspace_bytes, nullptr, stream);
+                  selected, lse, workspace, workspace_bytes, false, nullptr, nullptr, stream);
 }
 
 pqhsa_status pqhsa_dense_decode_step(const pqhsa_shape* shape, const uint16_t* q,
@@ -342,7 +361,7 @@ pqhsa_status pqhsa_dense_decode_step(const pqhsa_shape* shape, const uint16_t* q
                                      float* out, float* lse, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream) {
   return run_dense(shape, q, k_cache, v_cache, block_table, context_lens, out, lse, workspace,
-                   workspace_bytes, nullptr, stream);
+                   workspace_bytes, nullptr, nullptr, stream);
 }
 
 pqhsa_status pqhsa_decode_step_profiled(const pqhsa_shape* shape, const void* index_buf,
@@ -350,14 +369,28 @@ pqhsa_status pqhsa_decode_step_profiled(const pqhsa_shape* shape, const void* in
                                         const uint16_t* v_cache, const int32_t* block_table,
                                         const int32_t* context_lens, float* out,
                                         int32_t* selected, float* lse, void* workspace,
-                                        size_t workspace_bytes, int dense,
-                                        hipEvent_t* stage_events, hipStream_t stream) {
-  if (!stage_events) return PQHSA_ERR_INVALID_ARG;
-  if (dense)
-    return run_dense(shape, q, k_cache, v_cache, block_table, context_lens, out, lse, workspace,
-                     workspace_bytes, stage_events, stream);
-  return run_step(shape, index_buf, q, k_cache, v_cache, block_table, context_lens, out,
-                  selected, lse, workspace, workspace_bytes, stage_events, stream);
+                                        size_t workspace_bytes, int variant,
+                                        hipEvent_t* events, int32_t* n_kernels,
+                                        hipStream_t stream) {
+  if (!events) return PQHSA_ERR_INVALID_ARG;
+  int nk = 0;
+  pqhsa_status st;
+  switch (variant) {
+    case PQHSA_VARIANT_DEFAULT:
+    case PQHSA_VARIANT_STAGED:
+      st = run_step(shape, index_buf, q, k_cache, v_cache, block_table, context_lens, out,
+                    selected, lse, workspace, workspace_bytes, variant == PQHSA_VARIANT_STAGED,
+                    events, &nk, stream);
+      break;
+    case PQHSA_VARIANT_DENSE:
+      st = run_dense(shape, q, k_cache, v_cache, block_table, context_lens, out, lse, workspace,
+                     workspace_bytes, events, &nk, stream);
+      break;
+    default:
+      return PQHSA_ERR_INVALID_ARG;
+  }
+  if (n_kernels) *n_kernels = nk;
+  return st;
 }
 
 pqhsa_status pqhsa_workspace_layout(const pqhsa_shape* shape, int dense, pqhsa_ws_layout* out) {
@@ -367,6 +400,7 @@ pqhsa_status pqhsa_workspace_layout(const pqhsa_shape* shape, int dense, pqhsa_w
   const WsLayout l = ws_layout(d, dense != 0);
   out->lut = l.lut; out->qc = l.qc; out->keys = l.keys; out->bins = l.bins;
   out->rows = l.rows; out->n_rows = l.n_rows; out->partials = l.partials;
+  out->flags = l.fflags;
   out->n_exact_splits = d.n_exact_splits;
   out->n_bg_splits = d.n_bg_splits;
   out->n_parts = d.n_parts;

@@ -25,41 +25,6 @@
 
 namespace pqhsa {
 
-template <int G>
-struct AttnState {
-  float m[G], l[G], acc[G][8];
-};
-
-template <int G>
-__device__ __forceinline__ void attend_row(AttnState<G>& st, const float (&qv)[G][8], uint4 kw,
-                                           uint4 vw) {
-  const float kf[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
-                       bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
-  const float vf[8] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y),
-                       bf16_lo(vw.z), bf16_hi(vw.z), bf16_lo(vw.w), bf16_hi(vw.w)};
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float s = qv[g][0] * kf[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) s = fmaf(qv[g][i], kf[i], s);
-    s = row16_sum(s);
-    const float mn = fmaxf(st.m[g], s);
-    const float al = exp2f(st.m[g] - mn);
-    const float p = exp2f(s - mn);
-    st.l[g] = fmaf(st.l[g], al, p);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.acc[g][i] = fmaf(st.acc[g][i], al, p * vf[i]);
-    st.m[g] = mn;
-  }
-}
-
-// Scale factors that bring states with maxima m0 and m1 to their common max.
-__device__ __forceinline__ void lse_factors(float m0, float m1, float* M, float* a0, float* a1) {
-  *M = fmaxf(m0, m1);
-  *a0 = (m0 == -INFINITY) ? 0.0f : exp2f(m0 - *M);
-  *a1 = (m1 == -INFINITY) ? 0.0f : exp2f(m1 - *M);
-}
-
 // LDS of one attend block: staged row offsets, then the merge of 4 waves x G
 // heads x (m, l, acc[128]).
 template <int G>

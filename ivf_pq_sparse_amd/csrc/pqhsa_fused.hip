@@ -1,0 +1,959 @@
+// The whole PQ-HSA decode step as one kernel.
+//
+// PQ-HSA page (rit.work blog), section "How approximate estimates return the
+// discarded context": per KV head, every indexed token gets an approximate
+// logit from the IVF-PQ index (third paragraph); the best of them within the
+// budget are read from the paged cache and computed exactly, the others keep
+// their approximate weight in the shared normalisation (fourth paragraph) and
+// contribute through their cluster's mean value (fifth paragraph); the first
+// tokens, the recent window and the not yet indexed tokens stay exact (sixth
+// paragraph).  Partials are merged by the prefix/suffix law
+// O = (N_P + N_S) / (D_P + D_S) of the quant_prune_distill post on query reuse.
+//
+// The staged kernels (tables, scan, collect, select, attend, merge) spend most
+// of a 128K step at kernel boundaries: each boundary costs a launch gap and a
+// cold start.  Here P blocks own the clusters of one (b, h) and meet at two
+// per-head barriers:
+//
+//   phase 1  LUT of the G query heads into LDS; one wave per cluster computes
+//            the approximate logits of its entries, their keys, the
+//            cluster's (max, sum of exp2) bins and a 4096-bin histogram of
+//            the keys' top 12 bits, added to the head's global histogram.
+//   barrier  (histogram complete)
+//   phase 2  threshold bucket from the histogram; the block's entries above
+//            it are selected, those inside it are published as ties; the
+//            selected entries' weights are added to per-cluster sums.
+//   barrier  (counts and records complete)
+//   phase 3  every block resolves the tie bucket with the same radix select
+//            (52-bit composite: low key bits, then inverted position, so equal
+//            keys prefer the lower position), takes an even share of the exact
+//            rows (sink, selected, recent/tail) plus its own clusters'
+//            background terms, and writes one partial (m, l, acc[128]) per
+//            query head.  The last block of the head to finish merges the P
+//            partials into O and the log-sum-exp, writes the ascending selected
+//            positions if asked, and clears the head's counters and histogram
+//            for the next step.
+//
+// Cross-block data moves only through device-scope stores, loads and atomics
+// (coherent across XCDs without cache write-back or invalidation); a thread
+// waits for its own stores before its block arrives at a barrier.
+//
+// Residency: the grid is at most one block per CU (each block takes more than
+// half a CU's LDS), so on a device that runs nothing else every block is
+// resident at once and the barriers cannot deadlock; a block that arrives
+// early only waits for blocks that are already running.  (A cooperative
+// launch would guarantee the same but costs tens of µs per launch.)  If CUs
+// are withheld, waits are bounded in time: a wait that runs out sets bit 0 of
+// the workspace flags and the step goes on, so a call always finishes.
+#include "pqhsa_internal.hpp"
+
+namespace pqhsa {
+
+namespace {
+
+constexpr unsigned long long kBarrierTimeout = 200000000ull;   // 2 s of the 100 MHz clock
+
+template <int G>
+struct FusedCfg {
+  static constexpr int NT = G == 8 ? 512 : 1024;   // 128 VGPRs at 1024 threads, 256 at 512
+  static constexpr int NW = NT / 64;
+  static constexpr int NG = NT / 16;                // 16-lane row groups
+  static constexpr int kItemsPerGroup = 4;
+  static constexpr int kItems = NG * kItemsPerGroup;   // attention items staged per phase
+  static constexpr size_t kUBytes = (size_t)kM * kKsub * G * sizeof(float);   // LUT, then reuse
+  static constexpr size_t kHBytes = (size_t)kHistBins * sizeof(uint32_t);
+  static constexpr size_t kWBytes = (size_t)kFusedWselMax * sizeof(unsigned long long);
+  static constexpr size_t kQBytes = (size_t)kFusedWselMax * sizeof(float);
+  static constexpr size_t kDyn = kUBytes + kHBytes + kWBytes + kQBytes;
+  static constexpr int kTieCap = (int)(kUBytes / sizeof(unsigned long long));
+  static_assert((size_t)NW * G * (2 + kD) * sizeof(float) <= kUBytes, "merge arrays");
+  static_assert((size_t)kItems * sizeof(long long) + 4096 <= kHBytes, "item staging");
+};
+
+struct FusedStatic {
+  int sh[40];
+  uint32_t rh[256];
+  int res[4];
+  int apre[kMaxFusedP + 1];
+  int tpre[kMaxFusedP + 1];
+  int tbase[kMaxFusedP + 1];
+  int last;
+};
+
+// ---------------------------------------------------------------- device-scope memory
+__device__ __forceinline__ void st_dev(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_dev(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld_dev(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Wait until every memory operation this thread issued has completed
+// (s_waitcnt vmcnt(0)); no cache write-back or invalidation.
+__device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0xF70); }
+
+// All P blocks of a head arrive; returns when all have arrived or the time
+// bound has passed (then bit 0 of *flags is set).
+__device__ void head_barrier(uint32_t* ctr, uint32_t n, uint32_t* flags) {
+  wait_mem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long t0 = wall_clock64();
+    while (ld_dev(ctr) < n) {
+      __builtin_amdgcn_s_sleep(1);
+      if (wall_clock64() - t0 > kBarrierTimeout) {
+        __hip_atomic_fetch_or(flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Exclusive block scan of two per-thread counts; the block totals go to *ta, *tb.
+template <int NT>
+__device__ void block_scan2(int a, int b, int* oa, int* ob, int* ta, int* tb, int* sh) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int xa = a, xb = b;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ya = __shfl_up(xa, o), yb = __shfl_up(xb, o);
+    if (lane >= o) { xa += ya; xb += yb; }
+  }
+  if (lane == 63) { sh[wave] = xa; sh[NW + 1 + wave] = xb; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int ra = 0, rb = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int va = sh[w], vb = sh[NW + 1 + w];
+      sh[w] = ra; sh[NW + 1 + w] = rb;
+      ra += va; rb += vb;
+    }
+    sh[NW] = ra;
+    sh[2 * NW + 1] = rb;
+  }
+  __syncthreads();
+  *oa = sh[wave] + xa - a;
+  *ob = sh[NW + 1 + wave] + xb - b;
+  *ta = sh[NW];
+  *tb = sh[2 * NW + 1];
+  __syncthreads();
+}
+
+__device__ __forceinline__ unsigned long long tie_composite(unsigned long long rec) {
+  // rec = key << 32 | position
+  return composite52(make_uint4((uint32_t)(rec >> 32), (uint32_t)rec, 0u, 0u));
+}
+
+__device__ __forceinline__ unsigned long long to_fixed(float w) {
+  return (unsigned long long)(w * kFixScale + 0.5f);
+}
+
+// One background item: the cluster's summed unselected weight as a logit
+// s_g (base 2) and its mean value as the row's value (8 dims per lane).
+template <int G>
+__device__ __forceinline__ void attend_bg(AttnState<G>& st, const float* sg, uint4 m0, uint4 m1) {
+  const float mu[8] = {__uint_as_float(m0.x), __uint_as_float(m0.y), __uint_as_float(m0.z),
+                       __uint_as_float(m0.w), __uint_as_float(m1.x), __uint_as_float(m1.y),
+                       __uint_as_float(m1.z), __uint_as_float(m1.w)};
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float s = sg[g];
+    if (s == -INFINITY) continue;
+    const float mn = fmaxf(st.m[g], s);
+    const float al = exp2f(st.m[g] - mn);
+    const float p = exp2f(s - mn);
+    st.l[g] = fmaf(st.l[g], al, p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc[g][i] = fmaf(st.acc[g][i], al, p * mu[i]);
+    st.m[g] = mn;
+  }
+}
+
+// One exact row for the G query heads, with q kept as packed bf16 (the
+// scale is applied to the row sum).
+template <int G>
+__device__ __forceinline__ void attend_row_pk(AttnState<G>& st, const uint4 (&qp)[G], float scl,
+                                              uint4 kw, uint4 vw) {
+  const float kf[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
+                       bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
+  const float vf[8] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y),
+                       bf16_lo(vw.z), bf16_hi(vw.z), bf16_lo(vw.w), bf16_hi(vw.w)};
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint4 q = qp[g];
+    float s = bf16_lo(q.x) * kf[0];
+    s = fmaf(bf16_hi(q.x), kf[1], s);
+    s = fmaf(bf16_lo(q.y), kf[2], s);
+    s = fmaf(bf16_hi(q.y), kf[3], s);
+    s = fmaf(bf16_lo(q.z), kf[4], s);
+    s = fmaf(bf16_hi(q.z), kf[5], s);
+    s = fmaf(bf16_lo(q.w), kf[6], s);
+    s = fmaf(bf16_hi(q.w), kf[7], s);
+    s = row16_sum(s) * scl;
+    const float mn = fmaxf(st.m[g], s);
+    const float al = exp2f(st.m[g] - mn);
+    const float p = exp2f(s - mn);
+    st.l[g] = fmaf(st.l[g], al, p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc[g][i] = fmaf(st.acc[g][i], al, p * vf[i]);
+    st.m[g] = mn;
+  }
+}
+
+template <int G>
+struct FRound {
+  uint4 cw[2];
+  int pp[2];
+};
+
+}  // namespace
+
+template <int G>
+__global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
+  using C = FusedCfg<G>;
+  constexpr int NT = C::NT, NW = C::NW, NG = C::NG;
+  constexpr int PT = 2;   // 64-entry tiles per scan round
+  constexpr int kIB = 2;  // attention items whose loads are in flight together
+  extern __shared__ __align__(16) unsigned char dyn[];
+  __shared__ FusedStatic S;
+  float* lut = reinterpret_cast<float*>(dyn);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(dyn + C::kUBytes);
+  unsigned long long* wsel = reinterpret_cast<unsigned long long*>(dyn + C::kUBytes + C::kHBytes);
+  float* qcl = reinterpret_cast<float*>(dyn + C::kUBytes + C::kHBytes + C::kWBytes);   // [ncl][G]
+
+  const Dims& d = a.d;
+  const int P = d.fP;
+  const int BH = d.B * d.Hkv;
+  int bh, sub;
+  xcd_map(blockIdx.x, BH, P, &bh, &sub);
+  const int b = bh / d.Hkv, h = bh % d.Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c0 = min(d.L, sub * d.fcpb), c1 = min(d.L, c0 + d.fcpb), ncl = c1 - c0;
+  const int32_t* off = a.ix.list_off + (size_t)bh * (d.L + 1);
+  auto entry_at = [&](int c) { return min(max(off[c], 0), d.cap); };
+  const int E0 = entry_at(c0), E1 = max(E0, entry_at(c1));
+  const SeqInfo si = seq_info(d, a.ctx, a.ix.n_indexed, b);
+  uint32_t* sync = a.ws.fsync + (size_t)bh * 4;
+  uint32_t* ghist = a.ws.hist + (size_t)bh * kHistBins;
+  uint32_t* keys = a.ws.keys + (size_t)bh * d.cap;
+  float* qcg = a.ws.qc + (size_t)bh * d.L * G;
+  float* bins = a.ws.bins + (size_t)bh * d.L * G * 2;
+  const uint4* codes = reinterpret_cast<const uint4*>(a.ix.codes + (size_t)bh * d.cap * kM);
+  const int32_t* pos = a.ix.pos + (size_t)bh * d.cap;
+  const int32_t* ent_list = a.ix.ent_list + (size_t)bh * d.cap;
+  const float* cent = a.ix.centroids + (size_t)bh * d.L * kD;
+  const uint16_t* qh = a.q + ((size_t)b * d.Hq + h * G) * kD;
+  // per-head record arrays, indexed in entry space (block j writes from its
+  // first entry on): selected positions, tie records, tie weights and clusters
+  int32_t* fpos = reinterpret_cast<int32_t*>(a.ws.seg_above + (size_t)bh * d.cap);
+  unsigned long long* ftie = reinterpret_cast<unsigned long long*>(a.ws.seg_tie + (size_t)bh * d.cap);
+  float* ftw = a.ws.seg_w + (size_t)bh * d.cap * G;
+  int32_t* ftc = reinterpret_cast<int32_t*>(a.ws.seg_aw + (size_t)bh * d.cap * G);
+  int32_t* frows = a.ws.rows + (size_t)bh * d.cap;
+
+  // ======================================================= phase 1: LUT and scan
+  auto issue = [&](FRound<G>& r, int base, int e1) {
+#pragma unroll
+    for (int t = 0; t < PT; ++t) {
+      const int e = base + t * 64 + lane;
+      r.pp[t] = -1;
+      if (e < e1) {
+        r.cw[t] = codes[e];
+        r.pp[t] = pos[e];
+      }
+    }
+  };
+  // the wave's first round goes out before the tables are built
+  int c = c0 + wave;
+  int e0 = 0, e1 = 0;
+  FRound<G> rb[2];
+  if (c < c1) {
+    e0 = entry_at(c);
+    e1 = max(e0, entry_at(c + 1));
+    issue(rb[0], e0, e1);
+  }
+  {
+    // LUT[m][j][g] = scale*log2e * q_g^(m) . B_m[j]
+    for (int pair = tid; pair < kM * kKsub; pair += NT) {
+      const int m = pair >> 8, j = pair & (kKsub - 1);
+      const float* cw = a.ix.codebooks + (((size_t)bh * kM + m) * kKsub + j) * kDsub;
+      const float4 v0 = *reinterpret_cast<const float4*>(cw);
+      const float4 v1 = *reinterpret_cast<const float4*>(cw + 4);
+      const float cv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint4 w = *reinterpret_cast<const uint4*>(qh + g * kD + m * kDsub);
+        const float qs[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                             bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+        float sacc = (qs[0] * d.scale_log2) * cv[0];
+#pragma unroll
+        for (int i = 1; i < kDsub; ++i) sacc = fmaf(qs[i] * d.scale_log2, cv[i], sacc);
+        lut[pair * G + g] = sacc;
+      }
+    }
+    // QC of the block's clusters, one per 16-lane row: qc[c][g] =
+    // scale*log2e * q_g . C_c (8 dims per lane, DPP row sum)
+    const int l16r = tid & 15;
+    for (int cl = tid >> 4; cl < ncl; cl += NT / 16) {
+      const float* cp = cent + (size_t)(c0 + cl) * kD + l16r * 8;
+      const float4 v0 = *reinterpret_cast<const float4*>(cp);
+      const float4 v1 = *reinterpret_cast<const float4*>(cp + 4);
+      const float cv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint4 w = *reinterpret_cast<const uint4*>(qh + g * kD + l16r * 8);
+        const float qs[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                             bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+        float sacc = (qs[0] * d.scale_log2) * cv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) sacc = fmaf(qs[i] * d.scale_log2, cv[i], sacc);
+        sacc = row16_sum(sacc);
+        if (l16r == g) {
+          qcl[cl * G + g] = sacc;
+          qcg[(size_t)(c0 + cl) * G + g] = sacc;
+        }
+      }
+    }
+    for (int i = tid; i < kHistBins; i += NT) hist[i] = 0u;
+    for (int i = tid; i < ncl * G; i += NT) wsel[i] = 0ull;
+  }
+  __syncthreads();
+  float qc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) qc[g] = c < c1 ? qcl[(c - c0) * G + g] : 0.0f;
+
+  float mx[G], sm[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) { mx[g] = -INFINITY; sm[g] = 0.0f; }
+  int base = e0;
+  // one round of PT tiles; the next round (more of this cluster, or the first
+  // of the wave's next one) is issued before this one is computed
+  auto round = [&](FRound<G>& now, FRound<G>& nxt) {
+    int nc = c, nbase = base + 64 * PT, ne0 = e0, ne1 = e1;
+    const bool last = nbase >= e1;
+    if (last) {
+      nc = c + NW;
+      if (nc < c1) {
+        ne0 = entry_at(nc);
+        ne1 = max(ne0, entry_at(nc + 1));
+      }
+      nbase = ne0;
+    }
+    if (nc < c1) issue(nxt, nbase, ne1);
+    float s[PT][G];
+#pragma unroll
+    for (int t = 0; t < PT; ++t) {
+      const int p = now.pp[t];
+      const int e = base + t * 64 + lane;
+#pragma unroll
+      for (int g = 0; g < G; ++g) s[t][g] = -INFINITY;
+      if (p >= 0) {
+        float v[G];
+        entry_logits_lds<G>(lut, qc, now.cw[t], v);
+        float kappa = v[0];
+#pragma unroll
+        for (int g = 1; g < G; ++g) kappa = fmaxf(kappa, v[g]);
+        uint32_t key = 0;
+        if (p >= si.cand_beg && p < si.cand_end) {
+          key = order_key(kappa);
+          atomicAdd(&hist[key >> (32 - kHistBits)], 1u);
+#pragma unroll
+          for (int g = 0; g < G; ++g) s[t][g] = v[g];
+        }
+        keys[e] = key;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float rm = s[0][g];
+#pragma unroll
+      for (int t = 1; t < PT; ++t) rm = fmaxf(rm, s[t][g]);
+      const float Mn = fmaxf(mx[g], rm);
+      if (Mn != -INFINITY) {
+        float acc = sm[g] * __builtin_amdgcn_exp2f(mx[g] - Mn);
+#pragma unroll
+        for (int t = 0; t < PT; ++t) acc += __builtin_amdgcn_exp2f(s[t][g] - Mn);
+        sm[g] = acc;
+        mx[g] = Mn;
+      }
+    }
+    if (last) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float M = wave_max(mx[g]);
+        const float part = (mx[g] == -INFINITY) ? 0.0f : sm[g] * __builtin_amdgcn_exp2f(mx[g] - M);
+        const float Ssum = wave_sum(part);
+        if (lane == 0) {
+          bins[((size_t)c * G + g) * 2] = M;
+          bins[((size_t)c * G + g) * 2 + 1] = Ssum;
+        }
+        mx[g] = -INFINITY;
+        sm[g] = 0.0f;
+      }
+      if (nc < c1) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) qc[g] = qcl[(nc - c0) * G + g];
+      }
+    }
+    c = nc;
+    base = nbase;
+    e0 = ne0;
+    e1 = ne1;
+  };
+  while (c < c1) {
+    round(rb[0], rb[1]);
+    if (!(c < c1)) break;
+    round(rb[1], rb[0]);
+  }
+  __syncthreads();
+  for (int i = tid; i < kHistBins; i += NT) {
+    const uint32_t v = hist[i];
+    if (v) __hip_atomic_fetch_add(&ghist[i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  head_barrier(&sync[0], (uint32_t)P, a.ws.fflags);
+
+  // ======================================================= phase 2: threshold bucket
+  for (int i = tid; i < kHistBins; i += NT) hist[i] = ld_dev(&ghist[i]);
+  __syncthreads();
+  int beta, above_b, total;
+  find_threshold(hist, si.k, S.sh, &beta, &above_b, &total);
+  const bool any = min(si.k, total) > 0 && beta >= 0;
+  auto entry_w = [&](int e, int cl, float* w) {
+    const uint4 cw = codes[e];
+    float q[G], sv[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) q[g] = qcl[(cl - c0) * G + g];
+    entry_logits_lds<G>(lut, q, cw, sv);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      w[g] = __builtin_amdgcn_exp2f(sv[g] - bins[((size_t)cl * G + g) * 2]);
+  };
+  // the block's entries in chunks of NT*4 (4 consecutive per thread): count,
+  // one block scan, list the chosen entries in LDS in entry order, then
+  // process the list one entry per thread
+  constexpr int kPer = 4;
+  constexpr int kChunk = NT * kPer;
+  static_assert(kChunk * sizeof(int) <= C::kHBytes, "chunk list");
+  int* elist = reinterpret_cast<int*>(hist);   // above entries from the front, ties from the back
+  int na = 0, nt = 0;
+  if (any) {
+    for (int cb = E0; cb < E1; cb += kChunk) {
+      const int e_beg = cb + tid * kPer;
+      uint32_t kv[kPer];
+      int ca = 0, ct = 0;
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int e = e_beg + u;
+        kv[u] = e < E1 ? keys[e] : 0u;
+        const int bucket = (int)(kv[u] >> (32 - kHistBits));
+        ca += kv[u] != 0u && bucket > beta;
+        ct += kv[u] != 0u && bucket == beta;
+      }
+      int oa, ot, ta, tt;
+      block_scan2<NT>(ca, ct, &oa, &ot, &ta, &tt, S.sh);
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int bucket = (int)(kv[u] >> (32 - kHistBits));
+        if (kv[u] != 0u && bucket > beta) elist[oa++] = e_beg + u;
+        if (kv[u] != 0u && bucket == beta) elist[kChunk - 1 - ot++] = e_beg + u;
+      }
+      __syncthreads();
+      for (int i = tid; i < ta + tt; i += NT) {
+        const bool isA = i < ta;
+        const int li = isA ? i : i - ta;
+        const int e = isA ? elist[li] : elist[kChunk - 1 - li];
+        const int cl = min(max(ent_list[e], c0), c1 - 1);
+        const int p = pos[e];
+        float w[G];
+        entry_w(e, cl, w);
+        if (isA) {
+          st_dev(&fpos[E0 + na + li], p);
+#pragma unroll
+          for (int g = 0; g < G; ++g) atomicAdd(&wsel[(cl - c0) * G + g], to_fixed(w[g]));
+        } else {
+          const int slot = E0 + nt + li;
+          st_dev(&ftie[slot], ((unsigned long long)keys[e] << 32) | (uint32_t)p);
+#pragma unroll
+          for (int g = 0; g < G; ++g) ftw[(size_t)slot * G + g] = w[g];
+          ftc[slot] = cl;
+        }
+      }
+      na += ta;
+      nt += tt;
+      __syncthreads();
+    }
+  }
+  if (tid == 0)
+    st_dev(&a.ws.fcnt[(size_t)bh * kMaxFusedP + sub],
+           ((unsigned long long)(uint32_t)nt << 32) | (uint32_t)na);
+  head_barrier(&sync[1], (uint32_t)P, a.ws.fflags);
+
+  // ======================================================= phase 3: ties, rows, partials
+  if (tid < 64) {
+    unsigned long long v = 0;
+    if (tid < P) v = ld_dev(&a.ws.fcnt[(size_t)bh * kMaxFusedP + tid]);
+    const int ca = (int)(uint32_t)v, ct = (int)(v >> 32);
+    int xa = ca, xt = ct;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int ya = __shfl_up(xa, o), yt = __shfl_up(xt, o);
+      if (tid >= o) { xa += ya; xt += yt; }
+    }
+    if (tid < P) {
+      S.apre[tid] = xa - ca;
+      S.tpre[tid] = xt - ct;
+      S.tbase[tid] = entry_at(min(tid * d.fcpb, d.L));
+    }
+    if (tid == 63) { S.apre[P] = xa; S.tpre[P] = xt; }
+  }
+  __syncthreads();
+  const int n_above = S.apre[P], n_tie = S.tpre[P];
+  const int ksel = any ? min(si.k, n_above + n_tie) : 0;
+  const int r = max(ksel - n_above, 0);
+  unsigned long long* tcache = reinterpret_cast<unsigned long long*>(dyn);
+  const bool cached = n_tie <= C::kTieCap;
+  auto tie_slot = [&](int i) {
+    const int j = seg_of(S.tpre, P, i);
+    return S.tbase[j] + (i - S.tpre[j]);
+  };
+  auto tie_rec = [&](int i) -> unsigned long long {
+    return cached ? tcache[i] : ld_dev(&ftie[tie_slot(i)]);
+  };
+  if (r > 0 && cached)
+    for (int i = tid; i < n_tie; i += NT) tcache[i] = ld_dev(&ftie[tie_slot(i)]);
+  __syncthreads();
+  unsigned long long prefix = 0, mask = 0;
+  const bool all = r >= n_tie;
+  if (r > 0 && !all) {
+    int need = r;
+    for (int shift = 44;; shift -= 8) {
+      const int s = shift > 0 ? shift : 0;
+      const unsigned long long dm = shift >= 0 ? 0xffull : 0xfull;
+      for (int i = tid; i < 256; i += NT) S.rh[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < n_tie; i += NT) {
+        const unsigned long long cp = tie_composite(tie_rec(i));
+        if ((cp & mask) == prefix) atomicAdd(&S.rh[(cp >> s) & dm], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        int v4[4], sl = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int bin = 255 - (tid * 4 + i);
+          v4[i] = bin <= (int)dm ? (int)S.rh[bin] : 0;
+          sl += v4[i];
+        }
+        int x = sl;
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(x, o);
+          if (tid >= o) x += y;
+        }
+        int run = x - sl;
+        if (run < need && run + sl >= need) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (run < need && run + v4[i] >= need) {
+              S.res[0] = 255 - (tid * 4 + i);
+              S.res[1] = run;
+              S.res[2] = v4[i];
+            }
+            run += v4[i];
+          }
+        }
+      }
+      __syncthreads();
+      const int dig = S.res[0];
+      need -= S.res[1];
+      prefix |= (unsigned long long)dig << s;
+      mask |= dm << s;
+      const bool done = S.res[2] == need || s == 0;
+      __syncthreads();
+      if (done) break;
+    }
+  }
+  auto is_winner = [&](unsigned long long rec) {
+    return all || (tie_composite(rec) & mask) >= prefix;
+  };
+  // this block's rows of the head's exact list [sink | above | tie winners | recent]
+  const int n_rec = si.T - si.recent_beg;
+  const int R = si.ns + ksel + n_rec;
+  const int lo = (int)((long long)sub * R / P), hi = (int)((long long)(sub + 1) * R / P);
+  if (r > 0) {
+    int run = 0;
+    for (int base2 = 0; base2 < n_tie; base2 += NT) {
+      const int i = base2 + tid;
+      unsigned long long rec = 0;
+      bool win = false;
+      if (i < n_tie) {
+        rec = tie_rec(i);
+        win = is_winner(rec);
+      }
+      int ow, dummy, tw, td;
+      block_scan2<NT>(win, 0, &ow, &dummy, &tw, &td, S.sh);
+      if (win) {
+        const int row = si.ns + n_above + run + ow;
+        if (row >= lo && row < hi) frows[row] = (int32_t)(uint32_t)rec;
+        const int j = seg_of(S.tpre, P, i);
+        if (j == sub) {
+          const int slot = S.tbase[j] + (i - S.tpre[j]);
+          const int cl = min(max(ftc[slot], c0), c1 - 1);
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            atomicAdd(&wsel[(cl - c0) * G + g], to_fixed(ftw[(size_t)slot * G + g]));
+        }
+      }
+      run += tw;
+    }
+  }
+  for (int rr = lo + tid; rr < hi; rr += NT) {
+    int p;
+    if (rr < si.ns) {
+      p = rr;
+    } else if (rr < si.ns + n_above) {
+      const int s = rr - si.ns;
+      const int j = seg_of(S.apre, P, s);
+      p = ld_dev(&fpos[S.tbase[j] + (s - S.apre[j])]);
+    } else if (rr < si.ns + ksel) {
+      continue;
+    } else {
+      p = si.recent_beg + (rr - si.ns - ksel);
+    }
+    frows[rr] = p;
+  }
+  __syncthreads();
+  // background logits of the block's clusters: log2 of the unselected weight
+  // (relative to the cluster max) plus the max
+  float* sbg = reinterpret_cast<float*>(hist);
+  long long* ioff = reinterpret_cast<long long*>(dyn + C::kUBytes + 4096);
+  for (int i = tid; i < ncl * G; i += NT) {
+    const int cl = c0 + i / G, g = i % G;
+    const float M = bins[((size_t)cl * G + g) * 2];
+    const float wb = bins[((size_t)cl * G + g) * 2 + 1] - (float)wsel[i] * kFixInv;
+    sbg[i] = (wb > 0.0f && M != -INFINITY) ? M + log2f(wb) : -INFINITY;
+  }
+  // exact rows and background clusters as one item list through 16-lane groups
+  const int l16 = tid & 15, rg = tid >> 4;
+  uint4 qp[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) qp[g] = *reinterpret_cast<const uint4*>(qh + g * kD + l16 * 8);
+  AttnState<G> st;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    st.m[g] = -INFINITY;
+    st.l[g] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc[g][i] = 0.0f;
+  }
+  const int nr = hi - lo;
+  const int n_items = nr + ncl;
+  const int32_t* tab = a.table + (size_t)b * d.max_pages;
+  const uint16_t* kc = a.kc + l16 * 8;
+  const uint16_t* vc = a.vc + l16 * 8;
+  const float* means = a.ix.means + (size_t)bh * d.L * kD + l16 * 8;
+  for (int ph = 0; ph < n_items; ph += C::kItems) {
+    const int n = min(C::kItems, n_items - ph);
+    __syncthreads();
+    if (tid < n) {
+      const int it = ph + tid;
+      if (it < nr) {
+        const int p = min(max(frows[lo + it], 0), d.cap - 1);
+        int page = tab[p >> 4];
+        page = min(max(page, 0), d.num_pages - 1);
+        ioff[tid] = ((long long)(page * kPage + (p & (kPage - 1))) * d.Hkv + h) * kD;
+      } else {
+        ioff[tid] = -1 - (long long)(it - nr);
+      }
+    }
+    __syncthreads();
+    // the group's items two at a time: both loads out, then both computed
+#pragma unroll
+    for (int u0 = 0; u0 < C::kItemsPerGroup; u0 += kIB) {
+      uint4 kw[kIB], vw[kIB];
+#pragma unroll
+      for (int u = 0; u < kIB; ++u) {
+        const int j = rg + (u0 + u) * NG;
+        kw[u] = vw[u] = make_uint4(0, 0, 0, 0);
+        if (j < n) {
+          const long long o = ioff[j];
+          if (o >= 0) {
+            kw[u] = *reinterpret_cast<const uint4*>(kc + o);
+            vw[u] = *reinterpret_cast<const uint4*>(vc + o);
+          } else {
+            const float* mu = means + (size_t)(c0 + (int)(-1 - o)) * kD;
+            kw[u] = *reinterpret_cast<const uint4*>(mu);
+            vw[u] = *reinterpret_cast<const uint4*>(mu + 4);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kIB; ++u) {
+        const int j = rg + (u0 + u) * NG;
+        if (j < n) {
+          const long long o = ioff[j];
+          if (o >= 0) attend_row_pk<G>(st, qp, d.scale_log2, kw[u], vw[u]);
+          else attend_bg<G>(st, sbg + (int)(-1 - o) * G, kw[u], vw[u]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // merge the wave's 4 row groups, then the waves through LDS
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mo = __shfl_xor(st.m[g], o);
+      const float lo_ = __shfl_xor(st.l[g], o);
+      float M, a0, a1;
+      lse_factors(st.m[g], mo, &M, &a0, &a1);
+      st.l[g] = st.l[g] * a0 + lo_ * a1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float ao = __shfl_xor(st.acc[g][i], o);
+        st.acc[g][i] = st.acc[g][i] * a0 + ao * a1;
+      }
+      st.m[g] = M;
+    }
+  }
+  float* mlw = reinterpret_cast<float*>(dyn);           // [NW][G][2]
+  float* accw = mlw + NW * G * 2;                        // [NW][G][128]
+  if (lane < 16) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (l16 == 0) {
+        mlw[(wave * G + g) * 2] = st.m[g];
+        mlw[(wave * G + g) * 2 + 1] = st.l[g];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) accw[(wave * G + g) * kD + l16 * 8 + i] = st.acc[g][i];
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * kD; idx += NT) {
+    const int g = idx / kD, dim = idx % kD;
+    float M = -INFINITY;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mlw[(w * G + g) * 2]);
+    float L = 0.0f, A = 0.0f;
+    if (M != -INFINITY) {
+      for (int w = 0; w < NW; ++w) {
+        const float mw = mlw[(w * G + g) * 2];
+        const float f = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+        L = fmaf(f, mlw[(w * G + g) * 2 + 1], L);
+        A = fmaf(f, accw[(w * G + g) * kD + dim], A);
+      }
+    }
+    float* out = a.ws.fpart + (((size_t)bh * G + g) * kMaxFusedP + sub) * kPart;
+    st_dev(&out[4 + dim], A);
+    if (dim == 0) {
+      st_dev(&out[0], M);
+      st_dev(&out[1], L);
+    }
+  }
+  wait_mem();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t old =
+        __hip_atomic_fetch_add(&sync[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    S.last = old == (uint32_t)(P - 1);
+  }
+  __syncthreads();
+  if (!S.last) return;
+
+  // ======================================================= last block of the head
+  float* mlp = reinterpret_cast<float*>(hist);   // [G][P][2]
+  for (int i = tid; i < G * P; i += NT) {
+    const int g = i / P, j = i % P;
+    const float* pp = a.ws.fpart + (((size_t)bh * G + g) * kMaxFusedP + j) * kPart;
+    mlp[i * 2] = ld_dev(&pp[0]);
+    mlp[i * 2 + 1] = ld_dev(&pp[1]);
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * kD; idx += NT) {
+    const int g = idx / kD, dim = idx % kD;
+    float M = -INFINITY;
+    for (int j = 0; j < P; ++j) M = fmaxf(M, mlp[(g * P + j) * 2]);
+    float L = 0.0f, A = 0.0f;
+    if (M != -INFINITY) {
+      const float* pp = a.ws.fpart + ((size_t)bh * G + g) * kMaxFusedP * kPart + 4 + dim;
+      for (int j0 = 0; j0 < P; j0 += 16) {
+        float x[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) x[u] = (j0 + u < P) ? ld_dev(&pp[(size_t)(j0 + u) * kPart]) : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (j0 + u < P) {
+            const float mj = mlp[(g * P + j0 + u) * 2];
+            const float f = (mj == -INFINITY) ? 0.0f : exp2f(mj - M);
+            L = fmaf(f, mlp[(g * P + j0 + u) * 2 + 1], L);
+            A = fmaf(f, x[u], A);
+          }
+        }
+      }
+    }
+    const size_t bq = (size_t)b * d.Hq + h * G + g;
+    a.out[bq * kD + dim] = L > 0.0f ? A / L : 0.0f;
+    if (dim == 0 && a.lse) a.lse[bq] = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+  }
+  if (a.selected) {
+    // ascending selected positions through a bitmap over positions
+    uint32_t* bits = reinterpret_cast<uint32_t*>(dyn);
+    const int nw = d.nwords;
+    __syncthreads();
+    for (int i = tid; i < nw; i += NT) bits[i] = 0u;
+    __syncthreads();
+    for (int s = tid; s < n_above; s += NT) {
+      const int j = seg_of(S.apre, P, s);
+      const int p = ld_dev(&fpos[S.tbase[j] + (s - S.apre[j])]);
+      if (p >= 0 && p < d.cap) atomicOr(&bits[p >> 5], 1u << (p & 31));
+    }
+    if (r > 0) {
+      for (int i = tid; i < n_tie; i += NT) {
+        const unsigned long long rec = ld_dev(&ftie[tie_slot(i)]);
+        const int p = (int)(uint32_t)rec;
+        if (is_winner(rec) && p >= 0 && p < d.cap) atomicOr(&bits[p >> 5], 1u << (p & 31));
+      }
+    }
+    __syncthreads();
+    const int per = (nw + NT - 1) / NT;
+    const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(bits[w]);
+    int oc, dummy, tc, td;
+    block_scan2<NT>(cnt, 0, &oc, &dummy, &tc, &td, S.sh);
+    int32_t* selout = a.selected + (size_t)bh * a.max_sel;
+    int at = oc;
+    for (int w = w0; w < w1; ++w) {
+      uint32_t bw = bits[w];
+      while (bw) {
+        const int bit = __ffs(bw) - 1;
+        bw &= bw - 1;
+        if (at < a.max_sel) selout[at] = w * 32 + bit;
+        ++at;
+      }
+    }
+    for (int i = tc + tid; i < a.max_sel; i += NT) selout[i] = -1;
+  }
+  if (tid == 0) a.ws.n_rows[bh] = R;
+  // every block of the head is past both barriers and has read the histogram
+  for (int i = tid; i < kHistBins; i += NT) st_dev(&ghist[i], 0u);
+  if (tid == 0) {
+    st_dev(&sync[0], 0u);
+    st_dev(&sync[1], 0u);
+    st_dev(&sync[2], 0u);
+  }
+}
+
+// ---------------------------------------------------------------- host side
+namespace {
+
+struct FusedDeviceInfo {
+  int ready;        // 0 unknown, 1 known
+  int cus;
+  int occ[4];       // blocks per CU for G = 1, 2, 4, 8
+};
+
+constexpr int kMaxDevices = 64;
+FusedDeviceInfo g_info[kMaxDevices];
+
+int g_index(int G) { return G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3; }
+
+template <int G>
+hipError_t prepare_g(int* occ) {
+  using C = FusedCfg<G>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fused<G>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kDyn);
+  if (e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, k_fused<G>, C::NT, C::kDyn);
+}
+
+const FusedDeviceInfo* device_info() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  FusedDeviceInfo& fi = g_info[dev];
+  if (__atomic_load_n(&fi.ready, __ATOMIC_ACQUIRE)) return &fi;
+  FusedDeviceInfo t{};
+  if (hipDeviceGetAttribute(&t.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return nullptr;
+  if (prepare_g<1>(&t.occ[0]) != hipSuccess || prepare_g<2>(&t.occ[1]) != hipSuccess ||
+      prepare_g<4>(&t.occ[2]) != hipSuccess || prepare_g<8>(&t.occ[3]) != hipSuccess)
+    return nullptr;
+  t.ready = 1;
+  fi.cus = t.cus;
+  for (int i = 0; i < 4; ++i) fi.occ[i] = t.occ[i];
+  __atomic_store_n(&fi.ready, 1, __ATOMIC_RELEASE);
+  return &fi;
+}
+
+}  // namespace
+
+size_t fused_lds_bytes(int G) {
+  switch (G) {
+    case 1: return FusedCfg<1>::kDyn;
+    case 2: return FusedCfg<2>::kDyn;
+    case 4: return FusedCfg<4>::kDyn;
+    case 8: return FusedCfg<8>::kDyn;
+  }
+  return 0;
+}
+
+int fused_blocks_per_head(const Dims& d) {
+  const FusedDeviceInfo* fi = device_info();
+  if (!fi) return 0;
+  // one block per CU at most (LDS), so that the whole grid is resident at
+  // once whenever the device is not shared
+  if (fi->occ[g_index(d.G)] != 1) return 0;
+  const int BH = d.B * d.Hkv;
+  const long long total = (long long)fi->occ[g_index(d.G)] * fi->cus;
+  long long p0 = total / BH;
+  if (p0 > kMaxFusedP) p0 = kMaxFusedP;
+  if (p0 > d.L) p0 = d.L;
+  if (p0 < 1) return 0;
+  const int cpb = (int)((d.L + p0 - 1) / p0);
+  if ((long long)cpb * d.G > kFusedWselMax) return 0;
+  // the selected-position bitmap of the last block lives in LDS
+  const size_t lut_hist = (size_t)kM * kKsub * d.G * sizeof(float) + kHistBins * sizeof(uint32_t);
+  if ((size_t)d.nwords * 4 > lut_hist) return 0;
+  return (d.L + cpb - 1) / cpb;
+}
+
+template <int G>
+static hipError_t fused_g(const StepArgs& a, const Launch& l) {
+  using C = FusedCfg<G>;
+  return launch_kernel(k_fused<G>, dim3(a.d.B * a.d.Hkv * a.d.fP), dim3(C::NT), C::kDyn, l, a);
+}
+
+hipError_t launch_fused(const StepArgs& a, const Launch& l) {
+  switch (a.d.G) {
+    case 1: return fused_g<1>(a, l);
+    case 2: return fused_g<2>(a, l);
+    case 4: return fused_g<4>(a, l);
+    case 8: return fused_g<8>(a, l);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pqhsa

@@ -33,6 +33,8 @@ constexpr int kPhaseRows = 256;         // rows whose cache offsets are staged i
 constexpr int kBgWaves = 4;             // waves per background block
 constexpr int kBgBatch = 4;             // clusters whose loads a background wave issues together
 constexpr int kUploadChunk = 4096;      // tokens per counting-sort chunk
+constexpr int kMaxFusedP = 64;          // fused step: at most this many blocks per (b, h)
+constexpr int kFusedWselMax = 1024;     // fused step: clusters per block x G held in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFixScale = 1099511627776.0f;   // 2^40: fixed-point unit of selected weights
 constexpr float kFixInv = 1.0f / 1099511627776.0f;
@@ -51,6 +53,8 @@ struct Dims {
   int bg_per_wave;            // clusters per background wave (a multiple of 4)
   int n_parts;                // partials per (b, q head)
   int upload_chunks;          // counting-sort chunks per (b, h)
+  int fP;                     // fused step: blocks per (b, h) (0: the staged kernels run)
+  int fcpb;                   // fused step: clusters per block
 };
 
 struct IndexPtrs {
@@ -82,6 +86,11 @@ struct WsPtrs {
   int32_t* rows;       // [BH][cap] exact rows as physical cache rows (page * 16 + slot)
   int32_t* n_rows;     // [BH]
   float* partials;     // [B][Hq][n_parts][132]
+  // fused step only
+  uint32_t* fsync;     // [BH][4] arrivals at the two per-head barriers, finished blocks
+  uint32_t* fflags;    // [1] bit 0: a barrier wait timed out
+  unsigned long long* fcnt;  // [BH][kMaxFusedP] (above count | tie count << 32) per block
+  float* fpart;        // [BH][G][kMaxFusedP][132] one partial per block and query head
 };
 
 struct StepArgs {
@@ -229,6 +238,163 @@ __device__ __forceinline__ void entry_logits(const float* __restrict__ lut, cons
   }
 }
 
+// ---------------------------------------------------------------- scan helpers
+// LUT entry (m, code) of a G-interleaved table in LDS: byte offset code*4G
+// plus the subspace base m*256*4G, which the compiler folds into the LDS
+// instruction's immediate offset.
+template <int G, int M>
+__device__ __forceinline__ void lut_add(const float* lut, uint32_t code, float* s) {
+  const float* e = lut + M * kKsub * G + code * G;
+  if constexpr (G == 8) {
+    const float4 a = *reinterpret_cast<const float4*>(e);
+    const float4 c = *reinterpret_cast<const float4*>(e + 4);
+    s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+    s[4] += c.x; s[5] += c.y; s[6] += c.z; s[7] += c.w;
+  } else if constexpr (G == 4) {
+    const float4 a = *reinterpret_cast<const float4*>(e);
+    s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+  } else if constexpr (G == 2) {
+    const float2 a = *reinterpret_cast<const float2*>(e);
+    s[0] += a.x; s[1] += a.y;
+  } else {
+    s[0] += e[0];
+  }
+}
+
+// Same sum as entry_logits (same order: qc, then subspaces 0..15).
+template <int G>
+__device__ __forceinline__ void entry_logits_lds(const float* lut, const float* qc, uint4 cw,
+                                                 float* s) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) s[g] = qc[g];
+  lut_add<G, 0>(lut, cw.x & 0xffu, s);
+  lut_add<G, 1>(lut, (cw.x >> 8) & 0xffu, s);
+  lut_add<G, 2>(lut, (cw.x >> 16) & 0xffu, s);
+  lut_add<G, 3>(lut, cw.x >> 24, s);
+  lut_add<G, 4>(lut, cw.y & 0xffu, s);
+  lut_add<G, 5>(lut, (cw.y >> 8) & 0xffu, s);
+  lut_add<G, 6>(lut, (cw.y >> 16) & 0xffu, s);
+  lut_add<G, 7>(lut, cw.y >> 24, s);
+  lut_add<G, 8>(lut, cw.z & 0xffu, s);
+  lut_add<G, 9>(lut, (cw.z >> 8) & 0xffu, s);
+  lut_add<G, 10>(lut, (cw.z >> 16) & 0xffu, s);
+  lut_add<G, 11>(lut, cw.z >> 24, s);
+  lut_add<G, 12>(lut, cw.w & 0xffu, s);
+  lut_add<G, 13>(lut, (cw.w >> 8) & 0xffu, s);
+  lut_add<G, 14>(lut, (cw.w >> 16) & 0xffu, s);
+  lut_add<G, 15>(lut, cw.w >> 24, s);
+}
+
+// ---------------------------------------------------------------- threshold bucket
+// From the 4096-bin histogram of candidate keys (top 12 bits), find the bucket
+// holding the k-th largest key: beta with above(beta) < k <= above(beta) +
+// hist[beta], where above(x) counts keys in buckets > x.  Also returns the
+// total count.  Uses the whole block; blockDim is 256 or 1024.  sh must hold
+// blockDim/64 + 3 ints.
+__device__ inline void find_threshold(const uint32_t* __restrict__ gh, int k, int* sh, int* beta,
+                               int* above, int* total) {
+  const int nt = blockDim.x;
+  const int per = kHistBins / nt;
+  const int t = threadIdx.x;
+  // thread t owns bins [hi - per, hi), hi = 4096 - t*per (thread 0 has the top)
+  const int hi = kHistBins - t * per;
+  int v[16];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = i < per ? (int)gh[hi - 1 - i] : 0;
+    s += v[i];
+  }
+  const int lane = t & 63, wave = t >> 6, nw = nt >> 6;
+  int x = s;
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  if (t == 0) { sh[nw] = -1; sh[nw + 1] = 0; }
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int w = 0; w < nw; ++w) { int u = sh[w]; sh[w] = run; run += u; }
+    sh[nw + 2] = run;
+  }
+  __syncthreads();
+  const int tot = sh[nw + 2];
+  const int kk = min(k, tot);
+  const int before = sh[wave] + x - s;   // keys in bins above this thread's range
+  if (kk > 0 && before < kk && before + s >= kk) {
+    int run = before;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < per && run < kk) {
+        if (run + v[i] >= kk) { sh[nw] = hi - 1 - i; sh[nw + 1] = run; }
+        run += v[i];
+      }
+    }
+  }
+  __syncthreads();
+  *beta = sh[nw];
+  *above = sh[nw + 1];
+  *total = tot;
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- selection helpers
+// Radix-select composite of a threshold-bucket entry: the key's low 20 bits,
+// then the bit-inverted position, so that equal keys prefer the lower position.
+__device__ __forceinline__ unsigned long long composite52(uint4 c) {
+  return (((unsigned long long)c.x << 32) | (unsigned long long)(0xffffffffu - c.y)) &
+         0x000fffffffffffffull;
+}
+
+// Flat index i over the concatenated segments -> segment, given the exclusive
+// prefix pre[0..n] of segment sizes (pre[n] = total, i < total).
+__device__ __forceinline__ int seg_of(const int* pre, int n, int i) {
+  int lo = 0, hi = n;   // pre[lo] <= i < pre[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= i) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------- attention helpers
+template <int G>
+struct AttnState {
+  float m[G], l[G], acc[G][8];
+};
+
+template <int G>
+__device__ __forceinline__ void attend_row(AttnState<G>& st, const float (&qv)[G][8], uint4 kw,
+                                           uint4 vw) {
+  const float kf[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
+                       bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
+  const float vf[8] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y),
+                       bf16_lo(vw.z), bf16_hi(vw.z), bf16_lo(vw.w), bf16_hi(vw.w)};
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float s = qv[g][0] * kf[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) s = fmaf(qv[g][i], kf[i], s);
+    s = row16_sum(s);
+    const float mn = fmaxf(st.m[g], s);
+    const float al = exp2f(st.m[g] - mn);
+    const float p = exp2f(s - mn);
+    st.l[g] = fmaf(st.l[g], al, p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.acc[g][i] = fmaf(st.acc[g][i], al, p * vf[i]);
+    st.m[g] = mn;
+  }
+}
+
+// Scale factors that bring states with maxima m0 and m1 to their common max.
+__device__ __forceinline__ void lse_factors(float m0, float m1, float* M, float* a0, float* a1) {
+  *M = fmaxf(m0, m1);
+  *a0 = (m0 == -INFINITY) ? 0.0f : exp2f(m0 - *M);
+  *a1 = (m1 == -INFINITY) ? 0.0f : exp2f(m1 - *M);
+}
+
 // ---------------------------------------------------------------- launchers
 // Stream and optional timing events of one kernel launch.  With events the
 // launch goes through hipExtLaunchKernel, which stamps the two events with the
@@ -256,5 +422,10 @@ hipError_t launch_collect(const StepArgs& a, const Launch& l);
 hipError_t launch_select(const StepArgs& a, const Launch& l);
 hipError_t launch_exact_and_background(const StepArgs& a, bool dense, const Launch& l);
 hipError_t launch_merge(const StepArgs& a, const Launch& l);
+// Fused step: blocks per (b, h) that fit co-resident on the device (0 when the
+// fused kernel cannot run this shape), and its launch.
+int fused_blocks_per_head(const Dims& d);
+size_t fused_lds_bytes(int G);
+hipError_t launch_fused(const StepArgs& a, const Launch& l);
 
 }  // namespace pqhsa

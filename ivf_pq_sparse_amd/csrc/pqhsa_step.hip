@@ -89,52 +89,6 @@ __global__ __launch_bounds__(256) void k_tables(StepArgs a) {
 // running (max, sum of exp2) over candidates: one max over the round, then
 // one exp2 per value; the cluster's (max, sum) is reduced over the wave.
 
-// LUT entry (m, code) of a G-interleaved table in LDS: byte offset code*4G
-// plus the subspace base m*256*4G, which the compiler folds into the LDS
-// instruction's immediate offset.
-template <int G, int M>
-__device__ __forceinline__ void lut_add(const float* lut, uint32_t code, float* s) {
-  const float* e = lut + M * kKsub * G + code * G;
-  if constexpr (G == 8) {
-    const float4 a = *reinterpret_cast<const float4*>(e);
-    const float4 c = *reinterpret_cast<const float4*>(e + 4);
-    s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
-    s[4] += c.x; s[5] += c.y; s[6] += c.z; s[7] += c.w;
-  } else if constexpr (G == 4) {
-    const float4 a = *reinterpret_cast<const float4*>(e);
-    s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
-  } else if constexpr (G == 2) {
-    const float2 a = *reinterpret_cast<const float2*>(e);
-    s[0] += a.x; s[1] += a.y;
-  } else {
-    s[0] += e[0];
-  }
-}
-
-// Same sum as entry_logits (same order: qc, then subspaces 0..15).
-template <int G>
-__device__ __forceinline__ void entry_logits_lds(const float* lut, const float* qc, uint4 cw,
-                                                 float* s) {
-#pragma unroll
-  for (int g = 0; g < G; ++g) s[g] = qc[g];
-  lut_add<G, 0>(lut, cw.x & 0xffu, s);
-  lut_add<G, 1>(lut, (cw.x >> 8) & 0xffu, s);
-  lut_add<G, 2>(lut, (cw.x >> 16) & 0xffu, s);
-  lut_add<G, 3>(lut, cw.x >> 24, s);
-  lut_add<G, 4>(lut, cw.y & 0xffu, s);
-  lut_add<G, 5>(lut, (cw.y >> 8) & 0xffu, s);
-  lut_add<G, 6>(lut, (cw.y >> 16) & 0xffu, s);
-  lut_add<G, 7>(lut, cw.y >> 24, s);
-  lut_add<G, 8>(lut, cw.z & 0xffu, s);
-  lut_add<G, 9>(lut, (cw.z >> 8) & 0xffu, s);
-  lut_add<G, 10>(lut, (cw.z >> 16) & 0xffu, s);
-  lut_add<G, 11>(lut, cw.z >> 24, s);
-  lut_add<G, 12>(lut, cw.w & 0xffu, s);
-  lut_add<G, 13>(lut, (cw.w >> 8) & 0xffu, s);
-  lut_add<G, 14>(lut, (cw.w >> 16) & 0xffu, s);
-  lut_add<G, 15>(lut, cw.w >> 24, s);
-}
-
 template <int G, int P>
 struct ScanRound {
   uint4 cw[P];
@@ -306,61 +260,6 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(StepArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- threshold bucket
-// From the 4096-bin histogram of candidate keys (top 12 bits), find the bucket
-// holding the k-th largest key: beta with above(beta) < k <= above(beta) +
-// hist[beta], where above(x) counts keys in buckets > x.  Also returns the
-// total count.  Uses the whole block; blockDim is 256 or 1024.  sh must hold
-// blockDim/64 + 3 ints.
-__device__ void find_threshold(const uint32_t* __restrict__ gh, int k, int* sh, int* beta,
-                               int* above, int* total) {
-  const int nt = blockDim.x;
-  const int per = kHistBins / nt;
-  const int t = threadIdx.x;
-  // thread t owns bins [hi - per, hi), hi = 4096 - t*per (thread 0 has the top)
-  const int hi = kHistBins - t * per;
-  int v[16];
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[i] = i < per ? (int)gh[hi - 1 - i] : 0;
-    s += v[i];
-  }
-  const int lane = t & 63, wave = t >> 6, nw = nt >> 6;
-  int x = s;
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh[wave] = x;
-  if (t == 0) { sh[nw] = -1; sh[nw + 1] = 0; }
-  __syncthreads();
-  if (t == 0) {
-    int run = 0;
-    for (int w = 0; w < nw; ++w) { int u = sh[w]; sh[w] = run; run += u; }
-    sh[nw + 2] = run;
-  }
-  __syncthreads();
-  const int tot = sh[nw + 2];
-  const int kk = min(k, tot);
-  const int before = sh[wave] + x - s;   // keys in bins above this thread's range
-  if (kk > 0 && before < kk && before + s >= kk) {
-    int run = before;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < per && run < kk) {
-        if (run + v[i] >= kk) { sh[nw] = hi - 1 - i; sh[nw + 1] = run; }
-        run += v[i];
-      }
-    }
-  }
-  __syncthreads();
-  *beta = sh[nw];
-  *above = sh[nw + 1];
-  *total = tot;
-  __syncthreads();
-}
-
 // Approximate base-2 weights of an index entry relative to its cluster's
 // max (<= 1 for candidates: the max was taken over them in the scan).
 template <int G>
@@ -391,29 +290,13 @@ __device__ __forceinline__ int entry_cluster(const StepArgs& a, int bh, int e) {
 }
 
 // ---------------------------------------------------------------- select
-// Run by the last collect block of a (b, h) (256 threads).  Marks the
+// One block per (b, h), after the collect kernel.  Marks the
 // above-threshold positions in an LDS bitmap over positions, resolves the
 // threshold bucket exactly with an 8-bit radix select over 52-bit composites
 // (the key's low 20 bits, then the bit-inverted position, so equal keys prefer
 // the lower position), adds the tie winners' precomputed weights to their
 // clusters, then compacts the bitmap into the ascending exact-row list: sink
 // rows, selected rows, recent/tail rows.
-__device__ __forceinline__ unsigned long long composite52(uint4 c) {
-  return (((unsigned long long)c.x << 32) | (unsigned long long)(0xffffffffu - c.y)) &
-         0x000fffffffffffffull;
-}
-
-// Flat index i over the concatenated segments -> segment, given the exclusive
-// prefix pre[0..n] of segment sizes (pre[n] = total, i < total).
-__device__ __forceinline__ int seg_of(const int* pre, int n, int i) {
-  int lo = 0, hi = n;   // pre[lo] <= i < pre[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (pre[mid] <= i) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 constexpr int kWinCap = 2048;   // tie winners listed in LDS before their weight updates
 constexpr size_t kWselLdsBytes = 64 * 1024;   // per-cluster selected weights kept in LDS up to this
 
@@ -682,6 +565,9 @@ __device__ void select_head(const StepArgs& a, int bh, const SeqInfo& si, unsign
   if (selout)
     for (int i = nsel + tid; i < a.max_sel; i += nthr) selout[i] = -1;
   if (tid == 0) a.ws.n_rows[bh] = base_r + (si.T - rb);
+  // every collect block has read the histogram: leave it cleared (the fused
+  // step expects a zero histogram)
+  for (int i = tid; i < kHistBins; i += nthr) a.ws.hist[(size_t)bh * kHistBins + i] = 0u;
   if (wsel_lds) {
     unsigned long long* out = a.ws.wsel + (size_t)bh * nwsel;
     for (int i = tid; i < nwsel; i += nthr) out[i] = wacc[i];

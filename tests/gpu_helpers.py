@@ -26,8 +26,10 @@ def log(msg):
     print(msg, flush=True)
 
 
-def run_gpu(inp, dense=False, want_selected=True, page_seed=0, spare_pages=0, max_context=None):
-    """Stage `inp`, upload the index and run one step; return numpy results."""
+def run_gpu(inp, dense=False, want_selected=True, page_seed=0, spare_pages=0, max_context=None,
+            staged=False):
+    """Stage `inp`, upload the index and run one step; return numpy results.
+    staged=True runs the six staged kernels instead of the default path."""
     tens, kw = stage(inp, "cuda", page_seed=page_seed, spare_pages=spare_pages,
                      max_context=max_context)
     shape = pq.make_shape(**kw)
@@ -41,8 +43,9 @@ def run_gpu(inp, dense=False, want_selected=True, page_seed=0, spare_pages=0, ma
     dec.upload(tens["centroids"], tens["codebooks"], tens["list_ids"], tens["codes"],
                tens["n_indexed"], tens["v_cache"], tens["block_table"])
     out, sel, lse = dec.step(tens["q"], tens["k_cache"], tens["v_cache"], tens["block_table"],
-                             tens["context_lens"], selected=want_selected, lse=True)
+                             tens["context_lens"], selected=want_selected, lse=True, staged=staged)
     torch.cuda.synchronize()
+    assert dec.flags() == 0, "a barrier wait of the fused step timed out"
     res = dict(O=out.cpu().numpy().astype(np.float64), lse=lse.cpu().numpy(), shape=shape,
                dec=dec, tens=tens)
     if want_selected:
@@ -112,13 +115,14 @@ def oracle_with_details(inp, heads=None, background=True):
     return out
 
 
-def parity(inp, heads=None, what="", max_context=None, page_seed=0):
+def parity(inp, heads=None, what="", max_context=None, page_seed=0, staged=False):
     """Full check of one step: selection within band, outputs against the
     oracle recomputed with the GPU's set, and the log-sum-exp."""
     import oracle
     log(f"[parity] {what}: B={inp.batch} Hq={inp.num_q_heads} Hkv={inp.num_kv_heads} "
-        f"T={inp.context_lens.tolist()} L={inp.num_lists} bp={inp.budget_bp}")
-    g = run_gpu(inp, max_context=max_context, page_seed=page_seed)
+        f"T={inp.context_lens.tolist()} L={inp.num_lists} bp={inp.budget_bp} "
+        f"{'staged' if staged else 'default'}")
+    g = run_gpu(inp, max_context=max_context, page_seed=page_seed, staged=staged)
     ref = oracle_with_details(inp, heads=heads)
     nd = check_selection(g["selected"], ref, heads=heads)
     sel = {k: g["selected"][k] for k in ref["selected"]}

@@ -141,7 +141,10 @@ def test_null_pointers_and_small_buffers(lib, shape):
     assert lib.pqhsa_upload_index(S, fake, fake, fake, fake, fake, fake, fake, fake, ineed,
                                   fake, uneed - 1, None) == TOO_SMALL
     assert lib.pqhsa_decode_step_profiled(S, fake, fake, fake, fake, fake, fake, fake, None, None,
-                                          fake, 1 << 40, 0, None, None) == INVALID
+                                          fake, 1 << 40, 0, None, None, None) == INVALID
+    # an unknown variant is rejected before anything is read or launched
+    assert lib.pqhsa_decode_step_profiled(S, fake, fake, fake, fake, fake, fake, fake, None, None,
+                                          fake, 1 << 40, 7, fake, None, None) == INVALID
     assert lib.pqhsa_index_dropped(S, None, None, None) == INVALID
     assert lib.pqhsa_workspace_layout(S, 0, None) == INVALID
     assert lib.pqhsa_index_layout_of(None, None) == INVALID

@@ -161,12 +161,15 @@ def test_index_means_match_oracle():
     assert pq.index_dropped(shape, buf) == 0
 
 
-def test_tables_and_keys_match_oracle():
+@pytest.mark.parametrize("staged", [True, False])
+def test_tables_and_keys_match_oracle(staged):
+    # the staged path keeps the lookup table in the workspace; both paths keep
+    # the centroid terms and the keys
     import ivf_pq_sparse_amd as pq
     from oracle import pqhsa_oracle as orc
     inp = make_step_inputs(1, context_lens=[4000], num_q_heads=8, num_kv_heads=2, num_lists=24,
                            workload_id=31)
-    g = run_gpu(inp)
+    g = run_gpu(inp, staged=staged)
     shape, dec = g["shape"], g["dec"]
     lay = pq.workspace_layout(shape)
     ws = dec.workspace
@@ -174,13 +177,71 @@ def test_tables_and_keys_match_oracle():
     lut = ws[lay.lut:lay.lut + H * 16 * 256 * G * 4].view(torch.float32).cpu().numpy()
     lut = lut.reshape(H, 16, 256, G)
     qc = ws[lay.qc:lay.qc + H * L * G * 4].view(torch.float32).cpu().numpy().reshape(H, L, G)
+    cap = shape.max_context
+    keys = ws[lay.keys:lay.keys + H * cap * 4].view(torch.int32).cpu().numpy().view(np.uint32)
+    ilay = pq.index_layout(shape)
+    pos = dec.index[ilay.pos:ilay.pos + H * cap * 4].view(torch.int32).cpu().numpy()
     log2e = 1.0 / np.log(2.0)
+    Ti = int(inp.n_indexed[0])
+    F, Cand = orc.partition(int(inp.context_lens[0]), Ti, inp.n_sink, inp.n_recent)
     for h in range(H):
         q = orc.bf16_to_f64(inp.q_bits[0, h * G:(h + 1) * G])
         qc_ref, lut_ref = orc.lut_tables(q, inp.centroids[0, h].astype(np.float64),
                                          inp.codebooks[0, h].astype(np.float64), inp.scale)
-        np.testing.assert_allclose(lut[h], np.transpose(lut_ref, (1, 2, 0)) * log2e, atol=2e-6)
+        if staged:
+            np.testing.assert_allclose(lut[h], np.transpose(lut_ref, (1, 2, 0)) * log2e,
+                                       atol=2e-6)
         np.testing.assert_allclose(qc[h], qc_ref.T * log2e, atol=5e-6)
+        # keys: order-preserving bits of max_g s_hat * log2e, 0 for non-candidates
+        s = orc.approx_logits(qc_ref, lut_ref, inp.list_ids[0, h, :Ti], inp.codes[0, h, :Ti])
+        kap = s.max(axis=0) * log2e
+        p = pos[h * cap:h * cap + Ti]
+        u = keys[h * cap:h * cap + Ti]
+        iscand = np.isin(p, Cand)
+        assert np.all(u[~iscand] == 0)
+        f = u[iscand]
+        bits = np.where(f & 0x80000000, f & 0x7FFFFFFF, ~f).astype(np.uint32)
+        got = bits.view(np.float32).astype(np.float64)
+        np.testing.assert_allclose(got, kap[p[iscand]], atol=2e-5, rtol=2e-6)
+
+
+def test_default_and_staged_paths_agree():
+    # same tables in the same order: identical keys, so identical selections;
+    # outputs differ only by summation order
+    inp = make_step_inputs(2)
+    log("[pqhsa] 128K: default vs staged")
+    a = run_gpu(inp)
+    b = run_gpu(inp, staged=True)
+    for key in a["selected"]:
+        assert np.array_equal(a["selected"][key], b["selected"][key]), key
+    assert np.abs(a["O"] - b["O"]).max() < 2e-5
+    assert np.abs(a["lse"] - b["lse"]).max() < 2e-5
+
+
+def test_staged_kernels_match_oracle():
+    parity(make_step_inputs(1), what="workload 1, staged kernels", staged=True)
+    parity(make_step_inputs(4, context_lens=[70000], num_lists=256, workload_id=45),
+           what="G=8 at 70K, staged kernels", staged=True)
+
+
+def test_default_path_runs_one_kernel_on_the_workload_shapes():
+    import ivf_pq_sparse_amd as pq
+    from pqhsa_synth.device import stage
+    for wid in (0, 1):
+        inp = make_step_inputs(wid)
+        tens, kw = stage(inp, "cuda")
+        shape = pq.make_shape(**kw)
+        dec = pq.PQHSADecoder(shape)
+        dec.upload(tens["centroids"], tens["codebooks"], tens["list_ids"], tens["codes"],
+                   tens["n_indexed"], tens["v_cache"], tens["block_table"])
+        out = torch.empty(shape.batch, shape.num_q_heads, 128, device="cuda")
+        evs = [pq.HipEvent() for _ in range(2 * pq.NUM_STAGES)]
+        n = pq.decode_step_profiled(shape, dec.index, tens["q"], tens["k_cache"],
+                                    tens["v_cache"], tens["block_table"], tens["context_lens"],
+                                    out, dec.workspace, evs)
+        torch.cuda.synchronize()
+        assert n == 1, f"workload {wid}: {n} kernels"
+        assert evs[0].elapsed_ms(evs[1]) > 0
 
 
 def test_repeated_steps_are_deterministic():
