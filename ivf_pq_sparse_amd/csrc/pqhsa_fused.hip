@@ -55,7 +55,7 @@ constexpr unsigned long long kBarrierTimeout = 200000000ull;   // 2 s of the 100
 
 template <int G>
 struct FusedCfg {
-  static constexpr int NT = G == 8 ? 512 : 1024;   // 128 VGPRs at 1024 threads, 256 at 512
+  static constexpr int NT = 512;   // 8 waves: up to 256 VGPRs each
   static constexpr int NW = NT / 64;
   static constexpr int NG = NT / 16;                // 16-lane row groups
   static constexpr int kItemsPerGroup = 4;
@@ -136,11 +136,7 @@ template <int NT>
 __device__ void block_scan2(int a, int b, int* oa, int* ob, int* ta, int* tb, int* sh) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int xa = a, xb = b;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int ya = __shfl_up(xa, o), yb = __shfl_up(xb, o);
-    if (lane >= o) { xa += ya; xb += yb; }
-  }
+  const int xa = wave_incl_scan(a), xb = wave_incl_scan(b);
   if (lane == 63) { sh[wave] = xa; sh[NW + 1 + wave] = xb; }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -159,6 +155,43 @@ __device__ void block_scan2(int a, int b, int* oa, int* ob, int* ta, int* tb, in
   *ta = sh[NW];
   *tb = sh[2 * NW + 1];
   __syncthreads();
+}
+
+// One wave, over bins [lo, 4096) of a histogram in LDS (bin = top 12 bits of
+// the key): the bucket beta holding the k-th largest key counted from the top,
+// i.e. above(beta) < k <= above(beta) + hist[beta] with above(x) the count in
+// bins (x, 4096); k is first capped at the range's total.  Two levels: lane l
+// sums the 64 bins below 4096 - 64 l (lane 0 the highest; read in a rotated
+// order, free of bank conflicts), a wave scan and a ballot pick the lane whose
+// range crosses k, then the wave takes that range's 64 bins one per lane and
+// finds the bin the same way.  Writes beta (-1 if the capped k is 0),
+// above(beta) and the total to out[0..2].
+__device__ void wave_threshold(const uint32_t* hist, int lo, int k, int* out) {
+  const int lane = threadIdx.x & 63;
+  const int hi = kHistBins - 64 * lane;
+  int s = 0;
+  if (hi > lo) {
+#pragma unroll 16
+    for (int i = 0; i < 64; ++i) {
+      const int x = hi - 1 - ((i + lane) & 63);
+      s += x >= lo ? (int)hist[x] : 0;
+    }
+  }
+  const int inc = wave_incl_scan(s);
+  const int tot = __builtin_amdgcn_readlane(inc, 63);
+  const int kk = min(k, tot);
+  int beta = -1, above = 0;
+  if (kk > 0) {
+    const int L = __ffsll((long long)__ballot(inc >= kk)) - 1;
+    const int before = __shfl(inc, L) - __shfl(s, L);
+    const int x = kHistBins - 64 * L - 1 - lane;
+    const int v = x >= lo ? (int)hist[x] : 0;
+    const int inc2 = wave_incl_scan(v);
+    const int l2 = __ffsll((long long)__ballot(before + inc2 >= kk)) - 1;
+    beta = kHistBins - 64 * L - 1 - l2;
+    above = before + __shfl(inc2, l2) - __shfl(v, l2);
+  }
+  if (lane == 0) { out[0] = beta; out[1] = above; out[2] = tot; }
 }
 
 __device__ __forceinline__ unsigned long long tie_composite(unsigned long long rec) {
@@ -404,9 +437,9 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     if (last) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float M = wave_max(mx[g]);
+        const float M = wave_max_dpp(mx[g]);
         const float part = (mx[g] == -INFINITY) ? 0.0f : sm[g] * __builtin_amdgcn_exp2f(mx[g] - M);
-        const float Ssum = wave_sum(part);
+        const float Ssum = wave_sum_dpp(part);
         if (lane == 0) {
           bins[((size_t)c * G + g) * 2] = M;
           bins[((size_t)c * G + g) * 2 + 1] = Ssum;
@@ -430,18 +463,39 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     round(rb[1], rb[0]);
   }
   __syncthreads();
-  for (int i = tid; i < kHistBins; i += NT) {
-    const uint32_t v = hist[i];
-    if (v) __hip_atomic_fetch_add(&ghist[i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // The block's own threshold bucket beta_b: at least k of its keys lie in
+  // bins >= beta_b, so the head's threshold bucket is >= beta_b and the bins
+  // below cannot matter.  Only bins >= beta_b go to the head's histogram
+  // (fewer atomics on shared lines), and only those are read back.
+  if (wave == 0) wave_threshold(hist, 0, si.k, S.res);
+  __syncthreads();
+  const int beta_b = S.res[0];   // -1: no candidate in this block, or k = 0
+  // with fewer than k candidates of its own the block flushes every bin, and
+  // the head's threshold may lie below its bins: it then reads them all
+  const int read_lo = S.res[2] >= si.k ? beta_b : 0;
+  __syncthreads();
+  if (beta_b >= 0) {
+    for (int i = beta_b + tid; i < kHistBins; i += NT) {
+      const uint32_t v = hist[i];
+      if (v) __hip_atomic_fetch_add(&ghist[i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   head_barrier(&sync[0], (uint32_t)P, a.ws.fflags);
 
   // ======================================================= phase 2: threshold bucket
-  for (int i = tid; i < kHistBins; i += NT) hist[i] = ld_dev(&ghist[i]);
-  __syncthreads();
-  int beta, above_b, total;
-  find_threshold(hist, si.k, S.sh, &beta, &above_b, &total);
-  const bool any = min(si.k, total) > 0 && beta >= 0;
+  // the head's histogram from read_lo up: exact there, because every block
+  // with at least k candidates added all its bins >= its own beta_b <= beta,
+  // and every other block added all of its bins
+  int beta = -1;
+  if (beta_b >= 0) {
+    for (int i = read_lo + tid; i < kHistBins; i += NT) hist[i] = ld_dev(&ghist[i]);
+    __syncthreads();
+    if (wave == 0) wave_threshold(hist, read_lo, si.k, S.res);
+    __syncthreads();
+    beta = S.res[0];
+    __syncthreads();
+  }
+  const bool any = beta >= 0;
   auto entry_w = [&](int e, int cl, float* w) {
     const uint4 cw = codes[e];
     float q[G], sv[G];
@@ -455,7 +509,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   // the block's entries in chunks of NT*4 (4 consecutive per thread): count,
   // one block scan, list the chosen entries in LDS in entry order, then
   // process the list one entry per thread
-  constexpr int kPer = 4;
+  constexpr int kPer = 8;
   constexpr int kChunk = NT * kPer;
   static_assert(kChunk * sizeof(int) <= C::kHBytes, "chunk list");
   int* elist = reinterpret_cast<int*>(hist);   // above entries from the front, ties from the back
@@ -517,11 +571,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     unsigned long long v = 0;
     if (tid < P) v = ld_dev(&a.ws.fcnt[(size_t)bh * kMaxFusedP + tid]);
     const int ca = (int)(uint32_t)v, ct = (int)(v >> 32);
-    int xa = ca, xt = ct;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int ya = __shfl_up(xa, o), yt = __shfl_up(xt, o);
-      if (tid >= o) { xa += ya; xt += yt; }
-    }
+    const int xa = wave_incl_scan(ca), xt = wave_incl_scan(ct);
     if (tid < P) {
       S.apre[tid] = xa - ca;
       S.tpre[tid] = xt - ct;
@@ -531,7 +581,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   }
   __syncthreads();
   const int n_above = S.apre[P], n_tie = S.tpre[P];
-  const int ksel = any ? min(si.k, n_above + n_tie) : 0;
+  const int ksel = min(si.k, n_above + n_tie);
   const int r = max(ksel - n_above, 0);
   unsigned long long* tcache = reinterpret_cast<unsigned long long*>(dyn);
   const bool cached = n_tie <= C::kTieCap;
@@ -567,11 +617,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
           v4[i] = bin <= (int)dm ? (int)S.rh[bin] : 0;
           sl += v4[i];
         }
-        int x = sl;
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(x, o);
-          if (tid >= o) x += y;
-        }
+        const int x = wave_incl_scan(sl);
         int run = x - sl;
         if (run < need && run + sl >= need) {
 #pragma unroll

@@ -146,6 +146,51 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, false);
+}
+
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x141>(x));
+  x = fmaxf(x, dpp_f<0x140>(x));
+  return x;
+}
+
+// Sum and max over the 64 lanes without LDS traffic: DPP within each 16-lane
+// row, then the four row results through scalar reads (wave-uniform result).
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x = row16_sum(x);
+  const int b = __float_as_int(x);
+  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = row16_max(x);
+  const int b = __float_as_int(x);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)),
+                     __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)),
+                     __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each
+// 16-lane row (row_shr 1, 2, 4, 8; lanes shifted in from outside the row add
+// 0), then row_bcast:15 and row_bcast:31 carry the row totals upwards.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_i<0x111, 0xF>(x);
+  x += dpp_i<0x112, 0xF>(x);
+  x += dpp_i<0x114, 0xF>(x);
+  x += dpp_i<0x118, 0xF>(x);
+  x += dpp_i<0x142, 0xA>(x);
+  x += dpp_i<0x143, 0xC>(x);
+  return x;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
   return x;
