@@ -171,10 +171,12 @@ __device__ void wave_threshold(const uint32_t* hist, int lo, int k, int* out) {
   const int hi = kHistBins - 64 * lane;
   int s = 0;
   if (hi > lo) {
+    // x stays within [hi - 64, hi) inside the table: loads need no guard
 #pragma unroll 16
     for (int i = 0; i < 64; ++i) {
       const int x = hi - 1 - ((i + lane) & 63);
-      s += x >= lo ? (int)hist[x] : 0;
+      const int v = (int)hist[x];
+      s += x >= lo ? v : 0;
     }
   }
   const int inc = wave_incl_scan(s);
@@ -185,7 +187,8 @@ __device__ void wave_threshold(const uint32_t* hist, int lo, int k, int* out) {
     const int L = __ffsll((long long)__ballot(inc >= kk)) - 1;
     const int before = __shfl(inc, L) - __shfl(s, L);
     const int x = kHistBins - 64 * L - 1 - lane;
-    const int v = x >= lo ? (int)hist[x] : 0;
+    const int vx = (int)hist[x];
+    const int v = x >= lo ? vx : 0;
     const int inc2 = wave_incl_scan(v);
     const int l2 = __ffsll((long long)__ballot(before + inc2 >= kk)) - 1;
     beta = kHistBins - 64 * L - 1 - l2;
@@ -330,47 +333,92 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     issue(rb[0], e0, e1);
   }
   {
-    // LUT[m][j][g] = scale*log2e * q_g^(m) . B_m[j]
-    for (int pair = tid; pair < kM * kKsub; pair += NT) {
-      const int m = pair >> 8, j = pair & (kKsub - 1);
-      const float* cw = a.ix.codebooks + (((size_t)bh * kM + m) * kKsub + j) * kDsub;
-      const float4 v0 = *reinterpret_cast<const float4*>(cw);
-      const float4 v1 = *reinterpret_cast<const float4*>(cw + 4);
-      const float cv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    // LUT[m][j][g] = scale*log2e * q_g^(m) . B_m[j].  Every thread's codebook
+    // rows are loaded at once (codeword j = tid % 256, subspaces tid / 256 +
+    // step * i), while q is staged in LDS as scaled floats; then the dot
+    // products run from registers and LDS.
+    constexpr int kPairs = kM * kKsub / NT;
+    constexpr int kMStep = NT / kKsub;
+    static_assert(kPairs * NT == kM * kKsub && kMStep >= 1, "LUT pairs");
+    const int j = tid & (kKsub - 1), m0 = tid / kKsub;
+    float4 cb[kPairs][2];
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) {
+      const float* cw = a.ix.codebooks + (((size_t)bh * kM + m0 + kMStep * i) * kKsub + j) * kDsub;
+      cb[i][0] = *reinterpret_cast<const float4*>(cw);
+      cb[i][1] = *reinterpret_cast<const float4*>(cw + 4);
+    }
+    // the first cluster of this thread's 16-lane row for the QC pass
+    const int l16r = tid & 15;
+    float4 cen0 = make_float4(0.f, 0.f, 0.f, 0.f), cen1 = cen0;
+    if ((tid >> 4) < ncl) {
+      const float* cp = cent + (size_t)(c0 + (tid >> 4)) * kD + l16r * 8;
+      cen0 = *reinterpret_cast<const float4*>(cp);
+      cen1 = *reinterpret_cast<const float4*>(cp + 4);
+    }
+    float* qsl = reinterpret_cast<float*>(hist);   // scaled q [G][128] until the QC pass
+    if (tid < G * kD / 8) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qh + tid * 8);
+      const float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                          bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qsl[tid * 8 + i] = f[i] * d.scale_log2;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) {
+      const int m = m0 + kMStep * i;
+      const float cv[8] = {cb[i][0].x, cb[i][0].y, cb[i][0].z, cb[i][0].w,
+                           cb[i][1].x, cb[i][1].y, cb[i][1].z, cb[i][1].w};
+      float outv[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const uint4 w = *reinterpret_cast<const uint4*>(qh + g * kD + m * kDsub);
-        const float qs[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                             bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-        float sacc = (qs[0] * d.scale_log2) * cv[0];
+        const float* qq = qsl + g * kD + m * kDsub;
+        float sacc = qq[0] * cv[0];
 #pragma unroll
-        for (int i = 1; i < kDsub; ++i) sacc = fmaf(qs[i] * d.scale_log2, cv[i], sacc);
-        lut[pair * G + g] = sacc;
+        for (int t = 1; t < kDsub; ++t) sacc = fmaf(qq[t], cv[t], sacc);
+        outv[g] = sacc;
+      }
+      float* dst = lut + (m * kKsub + j) * G;
+      if constexpr (G == 8) {
+        reinterpret_cast<float4*>(dst)[0] = make_float4(outv[0], outv[1], outv[2], outv[3]);
+        reinterpret_cast<float4*>(dst)[1] = make_float4(outv[4], outv[5], outv[6], outv[7]);
+      } else if constexpr (G == 4) {
+        *reinterpret_cast<float4*>(dst) = make_float4(outv[0], outv[1], outv[2], outv[3]);
+      } else if constexpr (G == 2) {
+        *reinterpret_cast<float2*>(dst) = make_float2(outv[0], outv[1]);
+      } else {
+        dst[0] = outv[0];
       }
     }
     // QC of the block's clusters, one per 16-lane row: qc[c][g] =
     // scale*log2e * q_g . C_c (8 dims per lane, DPP row sum)
-    const int l16r = tid & 15;
     for (int cl = tid >> 4; cl < ncl; cl += NT / 16) {
-      const float* cp = cent + (size_t)(c0 + cl) * kD + l16r * 8;
-      const float4 v0 = *reinterpret_cast<const float4*>(cp);
-      const float4 v1 = *reinterpret_cast<const float4*>(cp + 4);
+      float4 v0 = cen0, v1 = cen1;
+      if (cl != (tid >> 4)) {
+        const float* cp = cent + (size_t)(c0 + cl) * kD + l16r * 8;
+        v0 = *reinterpret_cast<const float4*>(cp);
+        v1 = *reinterpret_cast<const float4*>(cp + 4);
+      }
       const float cv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      float qcv[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const uint4 w = *reinterpret_cast<const uint4*>(qh + g * kD + l16r * 8);
-        const float qs[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                             bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-        float sacc = (qs[0] * d.scale_log2) * cv[0];
+        const float* qq = qsl + g * kD + l16r * 8;
+        float sacc = qq[0] * cv[0];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) sacc = fmaf(qs[i] * d.scale_log2, cv[i], sacc);
-        sacc = row16_sum(sacc);
+        for (int t = 1; t < 8; ++t) sacc = fmaf(qq[t], cv[t], sacc);
+        qcv[g] = row16_sum(sacc);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
         if (l16r == g) {
-          qcl[cl * G + g] = sacc;
-          qcg[(size_t)(c0 + cl) * G + g] = sacc;
+          qcl[cl * G + g] = qcv[g];
+          qcg[(size_t)(c0 + cl) * G + g] = qcv[g];
         }
       }
     }
+    __syncthreads();   // the staged q is read for the last time above
     for (int i = tid; i < kHistBins; i += NT) hist[i] = 0u;
     for (int i = tid; i < ncl * G; i += NT) wsel[i] = 0ull;
   }
@@ -506,55 +554,60 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     for (int g = 0; g < G; ++g)
       w[g] = __builtin_amdgcn_exp2f(sv[g] - bins[((size_t)cl * G + g) * 2]);
   };
-  // the block's entries in chunks of NT*4 (4 consecutive per thread): count,
-  // one block scan, list the chosen entries in LDS in entry order, then
-  // process the list one entry per thread
-  constexpr int kPer = 8;
+  // The block's entries in chunks of NT*16 (entry cb + u*NT + tid to thread
+  // tid): count, one block scan, list the chosen entries in LDS (above ones
+  // first, each group in thread order), then record them one list entry per
+  // thread.  Entries beyond the list's capacity are recorded by their thread.
+  constexpr int kPer = 16;
   constexpr int kChunk = NT * kPer;
-  static_assert(kChunk * sizeof(int) <= C::kHBytes, "chunk list");
-  int* elist = reinterpret_cast<int*>(hist);   // above entries from the front, ties from the back
+  constexpr int kListCap = (int)(C::kHBytes / sizeof(int));
+  int* elist = reinterpret_cast<int*>(hist);
   int na = 0, nt = 0;
+  auto record = [&](int e, bool isA, int idx) {
+    const int cl = min(max(ent_list[e], c0), c1 - 1);
+    const int p = pos[e];
+    float w[G];
+    entry_w(e, cl, w);
+    if (isA) {
+      st_dev(&fpos[E0 + idx], p);
+#pragma unroll
+      for (int g = 0; g < G; ++g) atomicAdd(&wsel[(cl - c0) * G + g], to_fixed(w[g]));
+    } else {
+      const int slot = E0 + idx;
+      st_dev(&ftie[slot], ((unsigned long long)keys[e] << 32) | (uint32_t)p);
+#pragma unroll
+      for (int g = 0; g < G; ++g) ftw[(size_t)slot * G + g] = w[g];
+      ftc[slot] = cl;
+    }
+  };
   if (any) {
     for (int cb = E0; cb < E1; cb += kChunk) {
-      const int e_beg = cb + tid * kPer;
-      uint32_t kv[kPer];
+      uint32_t chosen = 0;   // bit u: entry u of this thread is above or in the bucket
       int ca = 0, ct = 0;
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
-        const int e = e_beg + u;
-        kv[u] = e < E1 ? keys[e] : 0u;
-        const int bucket = (int)(kv[u] >> (32 - kHistBits));
-        ca += kv[u] != 0u && bucket > beta;
-        ct += kv[u] != 0u && bucket == beta;
+        const int e = cb + u * NT + tid;
+        const uint32_t kv = e < E1 ? keys[e] : 0u;
+        const int bucket = (int)(kv >> (32 - kHistBits));
+        ca += kv != 0u && bucket > beta;
+        ct += kv != 0u && bucket == beta;
+        if (kv != 0u && bucket >= beta) chosen |= 1u << u;
       }
       int oa, ot, ta, tt;
       block_scan2<NT>(ca, ct, &oa, &ot, &ta, &tt, S.sh);
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int bucket = (int)(kv[u] >> (32 - kHistBits));
-        if (kv[u] != 0u && bucket > beta) elist[oa++] = e_beg + u;
-        if (kv[u] != 0u && bucket == beta) elist[kChunk - 1 - ot++] = e_beg + u;
+      while (chosen) {
+        const int u = __ffs(chosen) - 1;
+        chosen &= chosen - 1;
+        const int e = cb + u * NT + tid;
+        const bool isA = (int)(keys[e] >> (32 - kHistBits)) > beta;
+        const int li = isA ? oa++ : ta + ot++;
+        if (li < kListCap) elist[li] = e;
+        else record(e, isA, isA ? na + li : nt + li - ta);
       }
       __syncthreads();
-      for (int i = tid; i < ta + tt; i += NT) {
-        const bool isA = i < ta;
-        const int li = isA ? i : i - ta;
-        const int e = isA ? elist[li] : elist[kChunk - 1 - li];
-        const int cl = min(max(ent_list[e], c0), c1 - 1);
-        const int p = pos[e];
-        float w[G];
-        entry_w(e, cl, w);
-        if (isA) {
-          st_dev(&fpos[E0 + na + li], p);
-#pragma unroll
-          for (int g = 0; g < G; ++g) atomicAdd(&wsel[(cl - c0) * G + g], to_fixed(w[g]));
-        } else {
-          const int slot = E0 + nt + li;
-          st_dev(&ftie[slot], ((unsigned long long)keys[e] << 32) | (uint32_t)p);
-#pragma unroll
-          for (int g = 0; g < G; ++g) ftw[(size_t)slot * G + g] = w[g];
-          ftc[slot] = cl;
-        }
+      for (int li = tid; li < min(ta + tt, kListCap); li += NT) {
+        const bool isA = li < ta;
+        record(elist[li], isA, isA ? na + li : nt + li - ta);
       }
       na += ta;
       nt += tt;
@@ -594,6 +647,26 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   };
   if (r > 0 && cached)
     for (int i = tid; i < n_tie; i += NT) tcache[i] = ld_dev(&ftie[tie_slot(i)]);
+  // this block's rows of the head's exact list [sink | above | tie winners |
+  // recent]: every row but the winners is known already
+  const int n_rec = si.T - si.recent_beg;
+  const int R = si.ns + ksel + n_rec;
+  const int lo = (int)((long long)sub * R / P), hi = (int)((long long)(sub + 1) * R / P);
+  for (int rr = lo + tid; rr < hi; rr += NT) {
+    int p;
+    if (rr < si.ns) {
+      p = rr;
+    } else if (rr < si.ns + n_above) {
+      const int s = rr - si.ns;
+      const int j = seg_of(S.apre, P, s);
+      p = ld_dev(&fpos[S.tbase[j] + (s - S.apre[j])]);
+    } else if (rr < si.ns + ksel) {
+      continue;
+    } else {
+      p = si.recent_beg + (rr - si.ns - ksel);
+    }
+    frows[rr] = p;
+  }
   __syncthreads();
   unsigned long long prefix = 0, mask = 0;
   const bool all = r >= n_tie;
@@ -644,11 +717,32 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   auto is_winner = [&](unsigned long long rec) {
     return all || (tie_composite(rec) & mask) >= prefix;
   };
-  // this block's rows of the head's exact list [sink | above | tie winners | recent]
-  const int n_rec = si.T - si.recent_beg;
-  const int R = si.ns + ksel + n_rec;
-  const int lo = (int)((long long)sub * R / P), hi = (int)((long long)(sub + 1) * R / P);
-  if (r > 0) {
+  // tie winners: the rows of this block's share, and the weights of this
+  // block's own winners.  With the ties cached, each thread takes a
+  // contiguous run of them and one block scan places their rows.
+  if (r > 0 && cached) {
+    const int per = (n_tie + NT - 1) / NT;
+    const int i0 = min(n_tie, tid * per), i1 = min(n_tie, i0 + per);
+    int cw = 0;
+    for (int i = i0; i < i1; ++i) cw += is_winner(tcache[i]);
+    int ow, dummy, tw, td;
+    block_scan2<NT>(cw, 0, &ow, &dummy, &tw, &td, S.sh);
+    int wi = ow;
+    for (int i = i0; i < i1; ++i) {
+      const unsigned long long rec = tcache[i];
+      if (!is_winner(rec)) continue;
+      const int row = si.ns + n_above + wi++;
+      if (row >= lo && row < hi) frows[row] = (int32_t)(uint32_t)rec;
+      const int j = seg_of(S.tpre, P, i);
+      if (j == sub) {
+        const int slot = S.tbase[j] + (i - S.tpre[j]);
+        const int cl = min(max(ftc[slot], c0), c1 - 1);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          atomicAdd(&wsel[(cl - c0) * G + g], to_fixed(ftw[(size_t)slot * G + g]));
+      }
+    }
+  } else if (r > 0) {
     int run = 0;
     for (int base2 = 0; base2 < n_tie; base2 += NT) {
       const int i = base2 + tid;
@@ -674,21 +768,6 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       }
       run += tw;
     }
-  }
-  for (int rr = lo + tid; rr < hi; rr += NT) {
-    int p;
-    if (rr < si.ns) {
-      p = rr;
-    } else if (rr < si.ns + n_above) {
-      const int s = rr - si.ns;
-      const int j = seg_of(S.apre, P, s);
-      p = ld_dev(&fpos[S.tbase[j] + (s - S.apre[j])]);
-    } else if (rr < si.ns + ksel) {
-      continue;
-    } else {
-      p = si.recent_beg + (rr - si.ns - ksel);
-    }
-    frows[rr] = p;
   }
   __syncthreads();
   // background logits of the block's clusters: log2 of the unselected weight
