@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain device copy of known size (for counter scaling)")
+    p.add_argument("--sweep", choices=["configs", "budget", "context"],
+                   help="print a markdown table of a sweep instead of the JSON line")
     p.add_argument("--summarize-profile", nargs=4, metavar=("TRACE", "FETCH", "WRITE", "OUT"),
                    help="write the markdown summary of three rocprofv3 output folders and exit")
     p.add_argument("--profile-command", default="",
@@ -215,10 +217,158 @@ def kernel_of_stage(stage, G):
             "merge": "k_merge"}[stage]
 
 
+class Rig:
+    """Layer copies of one step's inputs on the GPU (each with its own page
+    permutation and index, together larger than the 256 MB Infinity Cache)
+    and timed loops over them."""
+
+    def __init__(self, inp, n_layers=0, exact_only=0, max_bytes=60e9):
+        import torch
+
+        import ivf_pq_sparse_amd as pq
+        from pqhsa_synth.device import stage
+        self.torch, self.pq = torch, pq
+        tens, kw = stage(inp, "cuda")
+        self.shape = pq.make_shape(**kw, exact_only=exact_only)
+        kv_bytes = 2 * tens["k_cache"].numel() * 2
+        self.kv_bytes = kv_bytes
+        n = n_layers or max(2, int(np.ceil(2.5 * 256e6 / (kv_bytes / 17.6 + 1))))
+        n = min(n, max(2, int(max_bytes // (kv_bytes + pq.index_bytes(self.shape)))))
+        self.n_layers = n
+        self.layers = []
+        g = torch.Generator(device="cpu").manual_seed(1234)
+        P = self.shape.num_pages
+        for _ in range(n):
+            perm = torch.randperm(P, generator=g).to("cuda")
+            kc = torch.empty_like(tens["k_cache"])
+            vc = torch.empty_like(tens["v_cache"])
+            kc[perm] = tens["k_cache"]
+            vc[perm] = tens["v_cache"]
+            bt = tens["block_table"].clone()
+            valid = bt >= 0
+            bt[valid] = perm[bt[valid].long()].to(torch.int32)
+            dec = pq.PQHSADecoder(self.shape)
+            dec.upload(tens["centroids"], tens["codebooks"], tens["list_ids"], tens["codes"],
+                       tens["n_indexed"], vc, bt)
+            self.layers.append(dict(kc=kc, vc=vc, bt=bt, dec=dec))
+        torch.cuda.synchronize()
+        del tens["k_cache"], tens["v_cache"]
+        self.q, self.ctx = tens["q"], tens["context_lens"]
+        self.ws = self.layers[0]["dec"].workspace
+        self.dense_ws = self.layers[0]["dec"].dense_workspace()
+        self.out = torch.empty(self.shape.batch, self.shape.num_q_heads, 128,
+                               dtype=torch.float32, device="cuda")
+
+    def step(self, i, dense=False, out=None):
+        pq, L_ = self.pq, self.layers[i % self.n_layers]
+        out = self.out if out is None else out
+        if dense:
+            pq.dense_decode_step(self.shape, self.q, L_["kc"], L_["vc"], L_["bt"], self.ctx, out,
+                                 self.dense_ws)
+        else:
+            pq.decode_step(self.shape, L_["dec"].index, self.q, L_["kc"], L_["vc"], L_["bt"],
+                           self.ctx, out, self.ws)
+
+    def timed(self, dense, steps, warmup):
+        """Average µs per step over `steps` steps after `warmup` untimed ones."""
+        torch, pq = self.torch, self.pq
+        for i in range(warmup):
+            self.step(i, dense)
+        torch.cuda.synchronize()
+        e0, e1 = pq.HipEvent(), pq.HipEvent()
+        stream = torch.cuda.current_stream()
+        e0.record(stream)
+        for i in range(steps):
+            self.step(i, dense)
+        e1.record(stream)
+        e1.synchronize()
+        torch.cuda.synchronize()
+        return e0.elapsed_ms(e1) / steps * 1e3
+
+
+def sweep(name, steps, warmup):
+    """Markdown tables on stdout (progress on stderr):
+      configs: every workload, PQ-HSA step and dense split-K step;
+      budget:  the 128K workload at budgets 0.25 % .. 100 %, with and without
+               the background term, time and output error against dense
+               attention on the same inputs;
+      context: the 128K workload's layer shape at 8K .. 512K tokens, PQ-HSA
+               vs dense split-K (where the index starts to pay)."""
+    import torch
+
+    import ivf_pq_sparse_amd as pq
+    from pqhsa_synth import WORKLOADS, make_step_inputs
+    pq.load()
+    rows = []
+    if name == "configs":
+        print("| workload | B x T | Hq/Hkv | L | k | PQ-HSA µs | dense µs | speed-up | "
+              "alg. MB | alg. GB/s |")
+        print("|---|---|---|---|---|---|---|---|---|---|")
+        for wid in range(5):
+            w = WORKLOADS[wid]
+            inp = make_step_inputs(wid)
+            rig = Rig(inp)
+            us = rig.timed(False, steps, warmup)
+            dus = rig.timed(True, steps, warmup)
+            k = -(-w["context"] * w["budget_bp"] // 10000)
+            n_rows = np.full(w["batch"] * w["num_kv_heads"],
+                             w["n_sink"] + k + max(w["n_recent"], w["n_tail"]))
+            tot, _ = algorithmic_bytes(inp, n_rows, np.full(n_rows.size, k), 1)
+            print(f"| {wid} {w['name']} | {w['batch']} x {w['context']} | "
+                  f"{w['num_q_heads']}/{w['num_kv_heads']} | {w['num_lists']} | {k} | "
+                  f"{us:.1f} | {dus:.1f} | {dus / us:.2f} | {tot / 1e6:.1f} | "
+                  f"{tot / (us * 1e-6) / 1e9:.0f} |", flush=True)
+            log(f"workload {wid}: {us:.1f} µs, dense {dus:.1f} µs ({rig.n_layers} copies)")
+            del rig
+            torch.cuda.empty_cache()
+    elif name == "budget":
+        inp = make_step_inputs(2)
+        print("| budget | background | PQ-HSA µs | dense µs | speed-up | max-abs err vs dense | "
+              "mean-rel err vs dense |")
+        print("|---|---|---|---|---|---|---|")
+        for bp in (25, 50, 100, 200, 500, 1000, 10000):
+            inp.budget_bp = bp
+            for eo in (0, 1):
+                rig = Rig(inp, n_layers=0, exact_only=eo)
+                us = rig.timed(False, steps, warmup)
+                dus = rig.timed(True, steps, warmup)
+                o_s = torch.empty_like(rig.out)
+                o_d = torch.empty_like(rig.out)
+                rig.step(0, False, o_s)
+                rig.step(0, True, o_d)
+                torch.cuda.synchronize()
+                err = (o_s - o_d).abs()
+                rel = float(err.sum() / o_d.abs().sum())
+                print(f"| {bp / 100:g} % | {'off' if eo else 'on'} | {us:.1f} | {dus:.1f} | "
+                      f"{dus / us:.2f} | {float(err.max()):.2e} | {rel:.2e} |", flush=True)
+                log(f"budget {bp} bp exact_only={eo}: {us:.1f} µs")
+                del rig
+                torch.cuda.empty_cache()
+    elif name == "context":
+        print("| context | L | k | PQ-HSA µs | dense µs | speed-up |")
+        print("|---|---|---|---|---|---|")
+        for T in (8192, 16384, 32768, 65536, 131072, 262144, 524288):
+            L = max(64, T // 256)
+            inp = make_step_inputs(2, context_lens=[T], num_lists=L)
+            rig = Rig(inp)
+            us = rig.timed(False, steps, warmup)
+            dus = rig.timed(True, steps, warmup)
+            k = -(-T * inp.budget_bp // 10000)
+            print(f"| {T} | {L} | {k} | {us:.1f} | {dus:.1f} | {dus / us:.2f} |", flush=True)
+            log(f"context {T}: {us:.1f} µs, dense {dus:.1f} µs")
+            del rig
+            torch.cuda.empty_cache()
+    else:
+        raise SystemExit(f"unknown sweep {name}")
+
+
 def main():
     args = parse()
     if args.summarize_profile:
         summarize_profile(*args.summarize_profile, command=args.profile_command)
+        return
+    if args.sweep:
+        sweep(args.sweep, args.steps, args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the PQ-HSA step "

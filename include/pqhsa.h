@@ -72,6 +72,11 @@ typedef struct pqhsa_shape {
   int32_t n_recent;           /* last tokens always attended exactly, >= 0 */
   int32_t budget_bp;          /* top-k budget in basis points of the context, 0..10000 */
   float scale;                /* logit scale, normally 1/sqrt(head_dim); > 0 */
+  int32_t exact_only;         /* 0: PQ-HSA (exact part + background term);
+                                 1: drop the background term, i.e. plain top-k
+                                 sparse attention over sink, selected and recent
+                                 tokens, the comparison of section B of the
+                                 PQ-HSA page; other values are invalid */
 } pqhsa_shape;
 
 /* Number of entry points computed per step (exact partial splits etc.) are

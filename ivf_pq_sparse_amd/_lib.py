@@ -33,7 +33,7 @@ class Shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "num_pages",
         "max_pages_per_seq", "num_lists", "pq_m", "pq_ksub", "max_context", "n_sink", "n_recent",
-        "budget_bp")] + [("scale", ctypes.c_float)]
+        "budget_bp")] + [("scale", ctypes.c_float), ("exact_only", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -97,10 +97,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
 # ------------------------------------------------------------------ helpers
 def make_shape(*, batch, num_q_heads, num_kv_heads, num_pages, max_pages_per_seq, max_context,
                num_lists=1, n_sink=0, n_recent=0, budget_bp=0, scale=None, head_dim=128,
-               page_size=16, pq_m=16, pq_ksub=256) -> Shape:
+               page_size=16, pq_m=16, pq_ksub=256, exact_only=0) -> Shape:
     return Shape(batch, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                  max_pages_per_seq, num_lists, pq_m, pq_ksub, max_context, n_sink, n_recent,
-                 budget_bp, 1.0 / math.sqrt(head_dim) if scale is None else scale)
+                 budget_bp, 1.0 / math.sqrt(head_dim) if scale is None else scale,
+                 int(exact_only))
 
 
 def _stream(stream) -> ctypes.c_void_p:

@@ -38,6 +38,7 @@ pqhsa_status validate(const pqhsa_shape* s, bool dense) {
   if (s->num_lists < 1 || s->pq_m < 1 || s->pq_ksub < 1) return PQHSA_ERR_INVALID_ARG;
   if (s->n_sink < 0 || s->n_recent < 0) return PQHSA_ERR_INVALID_ARG;
   if (s->budget_bp < 0 || s->budget_bp > 10000) return PQHSA_ERR_INVALID_ARG;
+  if (s->exact_only != 0 && s->exact_only != 1) return PQHSA_ERR_INVALID_ARG;
   if (s->num_lists > kMaxLists) return PQHSA_ERR_UNSUPPORTED;
   if (s->pq_m != kM || s->pq_ksub != kKsub) return PQHSA_ERR_UNSUPPORTED;
   if (s->max_context > kMaxSparseContext) return PQHSA_ERR_UNSUPPORTED;
@@ -63,6 +64,7 @@ Dims make_dims(const pqhsa_shape* s, bool dense) {
   d.n_sink = dense ? 0 : s->n_sink;
   d.n_recent = dense ? 0 : s->n_recent;
   d.budget_bp = dense ? 0 : s->budget_bp;
+  d.exact_only = dense ? 1 : s->exact_only;
   d.scale_log2 = (float)((double)s->scale * 1.4426950408889634);
   d.nwords = ceil_div(d.cap, 32);
   {

@@ -183,7 +183,8 @@ __device__ void background_block(const StepArgs& a, int bh, int split, AttendLds
   const int b = bh / d.Hkv, h = bh % d.Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int cw0 = (split * kBgWaves + wave) * d.bg_per_wave;
-  const int cw1 = min(d.L, cw0 + d.bg_per_wave);
+  // without the background term every background partial is empty
+  const int cw1 = d.exact_only ? cw0 : min(d.L, cw0 + d.bg_per_wave);
   float M[G], Lw[G], acc[G][2];
 #pragma unroll
   for (int g = 0; g < G; ++g) {

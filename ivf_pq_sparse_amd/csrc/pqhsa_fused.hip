@@ -794,7 +794,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     for (int i = 0; i < 8; ++i) st.acc[g][i] = 0.0f;
   }
   const int nr = hi - lo;
-  const int n_items = nr + ncl;
+  const int n_items = nr + (d.exact_only ? 0 : ncl);   // background items last
   const int32_t* tab = a.table + (size_t)b * d.max_pages;
   const uint16_t* kc = a.kc + l16 * 8;
   const uint16_t* vc = a.vc + l16 * 8;

@@ -43,6 +43,7 @@ constexpr float kFixInv = 1.0f / 1099511627776.0f;
 struct Dims {
   int B, Hq, Hkv, G, L, num_pages, max_pages, cap;
   int n_sink, n_recent, budget_bp;
+  int exact_only;             // 1: no background term
   float scale_log2;           // scale * log2(e): logits are kept in base 2
   int nwords;                 // ceil(cap / 32): words of a per-head bitmap
   int scan_blocks;            // scan blocks per (b, h)

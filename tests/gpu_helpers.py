@@ -27,12 +27,13 @@ def log(msg):
 
 
 def run_gpu(inp, dense=False, want_selected=True, page_seed=0, spare_pages=0, max_context=None,
-            staged=False):
+            staged=False, background=True):
     """Stage `inp`, upload the index and run one step; return numpy results.
-    staged=True runs the six staged kernels instead of the default path."""
+    staged=True runs the six staged kernels instead of the default path;
+    background=False sets exact_only (no background term)."""
     tens, kw = stage(inp, "cuda", page_seed=page_seed, spare_pages=spare_pages,
                      max_context=max_context)
-    shape = pq.make_shape(**kw)
+    shape = pq.make_shape(**kw, exact_only=0 if background else 1)
     dec = pq.PQHSADecoder(shape)
     if dense:
         out, lse = dec.dense(tens["q"], tens["k_cache"], tens["v_cache"], tens["block_table"],
@@ -115,18 +116,20 @@ def oracle_with_details(inp, heads=None, background=True):
     return out
 
 
-def parity(inp, heads=None, what="", max_context=None, page_seed=0, staged=False):
+def parity(inp, heads=None, what="", max_context=None, page_seed=0, staged=False,
+           background=True):
     """Full check of one step: selection within band, outputs against the
     oracle recomputed with the GPU's set, and the log-sum-exp."""
     import oracle
     log(f"[parity] {what}: B={inp.batch} Hq={inp.num_q_heads} Hkv={inp.num_kv_heads} "
         f"T={inp.context_lens.tolist()} L={inp.num_lists} bp={inp.budget_bp} "
-        f"{'staged' if staged else 'default'}")
-    g = run_gpu(inp, max_context=max_context, page_seed=page_seed, staged=staged)
-    ref = oracle_with_details(inp, heads=heads)
+        f"{'staged' if staged else 'default'}{'' if background else ' exact-only'}")
+    g = run_gpu(inp, max_context=max_context, page_seed=page_seed, staged=staged,
+                background=background)
+    ref = oracle_with_details(inp, heads=heads, background=background)
     nd = check_selection(g["selected"], ref, heads=heads)
     sel = {k: g["selected"][k] for k in ref["selected"]}
-    again = oracle.decode_step(inp, selected=sel, heads=heads)
+    again = oracle.decode_step(inp, selected=sel, heads=heads, background=background)
     G = inp.num_q_heads // inp.num_kv_heads
     todo = sorted(ref["selected"])
     rows = [(b, h * G + gg) for b, h in todo for gg in range(G)]

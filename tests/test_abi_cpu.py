@@ -84,7 +84,7 @@ def test_sizes_for_the_128k_layer(shape):
     ("pq_m", 8, UNSUPPORTED), ("pq_ksub", 16, UNSUPPORTED), ("budget_bp", 10001, INVALID),
     ("budget_bp", -1, INVALID), ("n_sink", -1, INVALID), ("n_recent", -2, INVALID),
     ("max_context", 131072 + 17, INVALID), ("scale", 0.0, INVALID), ("scale", float("nan"), INVALID),
-    ("num_pages", 0, INVALID),
+    ("num_pages", 0, INVALID), ("exact_only", 2, INVALID), ("exact_only", -1, INVALID),
 ])
 def test_invalid_shapes_are_rejected(lib, shape, field, value, expect):
     import ivf_pq_sparse_amd as pq

@@ -68,6 +68,21 @@ def test_qwen_512k_parity():
     parity(make_step_inputs(4), what="workload 4 (512K, 32q/4kv G=8, L1024, k=5243)")
 
 
+# Background term off (plain top-k sparse attention over sink, selected and
+# recent tokens): the comparison of the PQ-HSA page's section B.
+@pytest.mark.parametrize("staged", [False, True])
+def test_exact_only_matches_oracle(staged):
+    parity(make_step_inputs(1), what="workload 1, no background", staged=staged,
+           background=False)
+
+
+def test_exact_only_full_budget_is_dense():
+    import oracle
+    inp = make_step_inputs(1, context_lens=[4100], budget_bp=10000, num_lists=32, workload_id=9)
+    g = run_gpu(inp, background=False)
+    check_output(g["O"], oracle.dense_step(inp), "exact-only budget 100% vs dense")
+
+
 def test_full_budget_is_dense_on_gpu():
     import oracle
     inp = make_step_inputs(1, context_lens=[4100], budget_bp=10000, num_lists=32, workload_id=9)
