@@ -117,8 +117,9 @@ __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0xF70); 
 __device__ void head_barrier(uint32_t* ctr, uint32_t n, uint32_t* flags) {
   wait_mem();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 < n) {
+    // not the last to arrive: poll until the others have
     const unsigned long long t0 = wall_clock64();
     while (ld_dev(ctr) < n) {
       __builtin_amdgcn_s_sleep(1);
@@ -218,8 +219,8 @@ __device__ __forceinline__ void attend_bg(AttnState<G>& st, const float* sg, uin
     const float s = sg[g];
     if (s == -INFINITY) continue;
     const float mn = fmaxf(st.m[g], s);
-    const float al = exp2f(st.m[g] - mn);
-    const float p = exp2f(s - mn);
+    const float al = __builtin_amdgcn_exp2f(st.m[g] - mn);
+    const float p = __builtin_amdgcn_exp2f(s - mn);
     st.l[g] = fmaf(st.l[g], al, p);
 #pragma unroll
     for (int i = 0; i < 8; ++i) st.acc[g][i] = fmaf(st.acc[g][i], al, p * mu[i]);
@@ -249,8 +250,8 @@ __device__ __forceinline__ void attend_row_pk(AttnState<G>& st, const uint4 (&qp
     s = fmaf(bf16_hi(q.w), kf[7], s);
     s = row16_sum(s) * scl;
     const float mn = fmaxf(st.m[g], s);
-    const float al = exp2f(st.m[g] - mn);
-    const float p = exp2f(s - mn);
+    const float al = __builtin_amdgcn_exp2f(st.m[g] - mn);
+    const float p = __builtin_amdgcn_exp2f(s - mn);
     st.l[g] = fmaf(st.l[g], al, p);
 #pragma unroll
     for (int i = 0; i < 8; ++i) st.acc[g][i] = fmaf(st.acc[g][i], al, p * vf[i]);
@@ -886,7 +887,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     if (M != -INFINITY) {
       for (int w = 0; w < NW; ++w) {
         const float mw = mlw[(w * G + g) * 2];
-        const float f = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+        const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
         L = fmaf(f, mlw[(w * G + g) * 2 + 1], L);
         A = fmaf(f, accw[(w * G + g) * kD + dim], A);
       }
@@ -909,39 +910,49 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   if (!S.last) return;
 
   // ======================================================= last block of the head
-  float* mlp = reinterpret_cast<float*>(hist);   // [G][P][2]
-  for (int i = tid; i < G * P; i += NT) {
-    const int g = i / P, j = i % P;
-    const float* pp = a.ws.fpart + (((size_t)bh * G + g) * kMaxFusedP + j) * kPart;
-    mlp[i * 2] = ld_dev(&pp[0]);
-    mlp[i * 2 + 1] = ld_dev(&pp[1]);
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * kD; idx += NT) {
-    const int g = idx / kD, dim = idx % kD;
-    float M = -INFINITY;
-    for (int j = 0; j < P; ++j) M = fmaxf(M, mlp[(g * P + j) * 2]);
-    float L = 0.0f, A = 0.0f;
-    if (M != -INFINITY) {
-      const float* pp = a.ws.fpart + ((size_t)bh * G + g) * kMaxFusedP * kPart + 4 + dim;
-      for (int j0 = 0; j0 < P; j0 += 16) {
-        float x[16];
+  // every (head, dim) thread loads its column of the P partials (a wave's
+  // loads of one partial are contiguous) while the first G*P threads stage
+  // the (m, l) pairs in LDS
+  {
+    float* mlp = reinterpret_cast<float*>(hist);   // [G][P][2]
+    constexpr int kOut = (G * kD + NT - 1) / NT;    // outputs per thread
+    const float* pbase = a.ws.fpart + (size_t)bh * G * kMaxFusedP * kPart;
+    if (tid < G * P) {
+      const int g = tid / P, j = tid % P;
+      const float* pp = pbase + ((size_t)g * kMaxFusedP + j) * kPart;
+      mlp[tid * 2] = ld_dev(&pp[0]);
+      mlp[tid * 2 + 1] = ld_dev(&pp[1]);
+    }
+    for (int o = 0; o < kOut; ++o) {
+      // threads past the outputs load a valid column and discard it
+      const int idx = min(tid + o * NT, G * kD - 1);
+      const int g = idx / kD, dim = idx % kD;
+      const float* col = pbase + (size_t)g * kMaxFusedP * kPart + 4 + dim;
+      float x[kMaxFusedP];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) x[u] = (j0 + u < P) ? ld_dev(&pp[(size_t)(j0 + u) * kPart]) : 0.0f;
+      for (int j = 0; j < kMaxFusedP; ++j) x[j] = j < P ? ld_dev(&col[(size_t)j * kPart]) : 0.0f;
+      __syncthreads();
+      if (tid + o * NT < G * kD) {
+        float M = -INFINITY;
+        for (int j = 0; j < P; ++j) M = fmaxf(M, mlp[(g * P + j) * 2]);
+        float L = 0.0f, A = 0.0f;
+        if (M != -INFINITY) {
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          if (j0 + u < P) {
-            const float mj = mlp[(g * P + j0 + u) * 2];
-            const float f = (mj == -INFINITY) ? 0.0f : exp2f(mj - M);
-            L = fmaf(f, mlp[(g * P + j0 + u) * 2 + 1], L);
-            A = fmaf(f, x[u], A);
+          for (int j = 0; j < kMaxFusedP; ++j) {
+            if (j < P) {
+              const float mj = mlp[(g * P + j) * 2];
+              const float f = (mj == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mj - M);
+              L = fmaf(f, mlp[(g * P + j) * 2 + 1], L);
+              A = fmaf(f, x[j], A);
+            }
           }
         }
+        const size_t bq = (size_t)b * d.Hq + h * G + g;
+        a.out[bq * kD + dim] = L > 0.0f ? A / L : 0.0f;
+        if (dim == 0 && a.lse)
+          a.lse[bq] = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
       }
     }
-    const size_t bq = (size_t)b * d.Hq + h * G + g;
-    a.out[bq * kD + dim] = L > 0.0f ? A / L : 0.0f;
-    if (dim == 0 && a.lse) a.lse[bq] = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
   }
   if (a.selected) {
     // ascending selected positions through a bitmap over positions
@@ -1056,6 +1067,10 @@ int fused_blocks_per_head(const Dims& d) {
   long long p0 = total / BH;
   if (p0 > kMaxFusedP) p0 = kMaxFusedP;
   if (p0 > d.L) p0 = d.L;
+  // no more blocks than about 1024 index entries each: below that the scan is
+  // short and every extra block only adds a partial to merge
+  const long long by_work = ((long long)d.cap + 1023) / 1024;
+  if (p0 > by_work) p0 = by_work;
   if (p0 < 1) return 0;
   const int cpb = (int)((d.L + p0 - 1) / p0);
   if ((long long)cpb * d.G > kFusedWselMax) return 0;
