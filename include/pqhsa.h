@@ -162,7 +162,7 @@ pqhsa_status pqhsa_index_dropped(const pqhsa_shape* shape, const void* index_buf
  * over the group's query heads, the overlap of the recent window with the
  * tail, and the tie rule are readings where the page is silent.)
  */
-/* Execution: when its grid fits the device at one block per CU, the step
+/* Execution: when its whole grid fits on the device at once, the step
  * runs as one kernel whose blocks of a KV head share that head's clusters and
  * meet at two barriers (fused step); otherwise as the six kernels listed
  * below (staged step).  Both compute the same quantities.  The fused step

@@ -38,10 +38,10 @@
 // (coherent across XCDs without cache write-back or invalidation); a thread
 // waits for its own stores before its block arrives at a barrier.
 //
-// Residency: the grid is at most one block per CU (each block takes more than
-// half a CU's LDS), so on a device that runs nothing else every block is
-// resident at once and the barriers cannot deadlock; a block that arrives
-// early only waits for blocks that are already running.  (A cooperative
+// Residency: the grid is at most as large as the device holds at once (blocks
+// per CU by occupancy times CUs), so on a device that runs nothing else every
+// block is resident at once and the barriers cannot deadlock; a block that
+// arrives early only waits for blocks that are already running.  (A cooperative
 // launch would guarantee the same but costs tens of µs per launch.)  If CUs
 // are withheld, waits are bounded in time: a wait that runs out sets bit 0 of
 // the workspace flags and the step goes on, so a call always finishes.
@@ -259,10 +259,10 @@ __device__ __forceinline__ void attend_row_pk(AttnState<G>& st, const uint4 (&qp
   }
 }
 
-template <int G>
+template <int G, int PT>
 struct FRound {
-  uint4 cw[2];
-  int pp[2];
+  uint4 cw[PT];
+  int pp[PT];
 };
 
 }  // namespace
@@ -271,7 +271,7 @@ template <int G>
 __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   using C = FusedCfg<G>;
   constexpr int NT = C::NT, NW = C::NW, NG = C::NG;
-  constexpr int PT = 2;   // 64-entry tiles per scan round
+  constexpr int PT = 4;   // 64-entry tiles per scan round
   constexpr int kIB = 2;  // attention items whose loads are in flight together
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ FusedStatic S;
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   int32_t* frows = a.ws.rows + (size_t)bh * d.cap;
 
   // ======================================================= phase 1: LUT and scan
-  auto issue = [&](FRound<G>& r, int base, int e1) {
+  auto issue = [&](FRound<G, PT>& r, int base, int e1) {
 #pragma unroll
     for (int t = 0; t < PT; ++t) {
       const int e = base + t * 64 + lane;
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   // the wave's first round goes out before the tables are built
   int c = c0 + wave;
   int e0 = 0, e1 = 0;
-  FRound<G> rb[2];
+  FRound<G, PT> rb[2];
   if (c < c1) {
     e0 = entry_at(c);
     e1 = max(e0, entry_at(c + 1));
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   int base = e0;
   // one round of PT tiles; the next round (more of this cluster, or the first
   // of the wave's next one) is issued before this one is computed
-  auto round = [&](FRound<G>& now, FRound<G>& nxt) {
+  auto round = [&](FRound<G, PT>& now, FRound<G, PT>& nxt) {
     int nc = c, nbase = base + 64 * PT, ne0 = e0, ne1 = e1;
     const bool last = nbase >= e1;
     if (last) {
@@ -1058,10 +1058,7 @@ size_t fused_lds_bytes(int G) {
 
 int fused_blocks_per_head(const Dims& d) {
   const FusedDeviceInfo* fi = device_info();
-  if (!fi) return 0;
-  // one block per CU at most (LDS), so that the whole grid is resident at
-  // once whenever the device is not shared
-  if (fi->occ[g_index(d.G)] != 1) return 0;
+  if (!fi || fi->occ[g_index(d.G)] < 1) return 0;
   const int BH = d.B * d.Hkv;
   const long long total = (long long)fi->occ[g_index(d.G)] * fi->cus;
   long long p0 = total / BH;
