@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain device copy of known size (for counter scaling)")
-    p.add_argument("--sweep", choices=["configs", "budget", "context"],
+    p.add_argument("--sweep", choices=["configs", "budget", "context", "append"],
                    help="print a markdown table of a sweep instead of the JSON line")
     p.add_argument("--summarize-profile", nargs=4, metavar=("TRACE", "FETCH", "WRITE", "OUT"),
                    help="write the markdown summary of three rocprofv3 output folders and exit")
@@ -293,7 +293,9 @@ def sweep(name, steps, warmup):
                the background term, time and output error against dense
                attention on the same inputs;
       context: the 128K workload's layer shape at 8K .. 512K tokens, PQ-HSA
-               vs dense split-K (where the index starts to pay)."""
+               vs dense split-K (where the index starts to pay);
+      append:  index build (whole upload) and update (appending a batch of
+               new tokens) at the 128K workload's shape."""
     import torch
 
     import ivf_pq_sparse_amd as pq
@@ -357,6 +359,52 @@ def sweep(name, steps, warmup):
             print(f"| {T} | {L} | {k} | {us:.1f} | {dus:.1f} | {dus / us:.2f} |", flush=True)
             log(f"context {T}: {us:.1f} µs, dense {dus:.1f} µs")
             del rig
+            torch.cuda.empty_cache()
+    elif name == "append":
+        # index build (upload of the whole index) and update (append of a
+        # batch of new tokens) at the 128K workload's shape
+        from pqhsa_synth.device import stage
+        print("| operation | tokens per (seq, KV head) | µs | µs per token per KV head |")
+        print("|---|---|---|---|")
+        for nb in (0, 16, 64, 256, 1024, 4096):
+            inp = make_step_inputs(2, n_tail=max(nb, 256))
+            tens, kw = stage(inp, "cuda")
+            shape = pq.make_shape(**kw)
+            dec = pq.PQHSADecoder(shape)
+            Hkv = shape.num_kv_heads
+            T = int(inp.context_lens[0])
+            e0, e1 = pq.HipEvent(), pq.HipEvent()
+            stream = torch.cuda.current_stream()
+            times = []
+            for rep in range(6):
+                lists = tens["list_ids"].clone()
+                codes = tens["codes"].clone()
+                if nb == 0:
+                    n_full = torch.tensor(inp.context_lens, dtype=torch.int32, device="cuda")
+                    torch.cuda.synchronize()
+                    e0.record(stream)
+                    dec.upload(tens["centroids"], tens["codebooks"], lists, codes, n_full,
+                               tens["v_cache"], tens["block_table"])
+                    e1.record(stream)
+                else:
+                    n_old = torch.tensor([T - nb], dtype=torch.int32, device="cuda")
+                    n_new = torch.tensor([T], dtype=torch.int32, device="cuda")
+                    dec.upload(tens["centroids"], tens["codebooks"], lists, codes, n_old,
+                               tens["v_cache"], tens["block_table"])
+                    torch.cuda.synchronize()
+                    e0.record(stream)
+                    dec.append(tens["k_cache"], tens["v_cache"], tens["block_table"], n_new,
+                               nb, lists, codes)
+                    e1.record(stream)
+                e1.synchronize()
+                if rep:
+                    times.append(e0.elapsed_ms(e1) * 1e3)
+            us = float(np.median(times))
+            what = "upload (build, all tokens)" if nb == 0 else "append"
+            ntok = T if nb == 0 else nb
+            print(f"| {what} | {ntok} | {us:.1f} | {us / ntok / Hkv:.4f} |", flush=True)
+            log(f"{what} {ntok}: {us:.1f} µs")
+            del dec, tens
             torch.cuda.empty_cache()
     else:
         raise SystemExit(f"unknown sweep {name}")

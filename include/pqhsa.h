@@ -129,6 +129,43 @@ pqhsa_status pqhsa_upload_index(const pqhsa_shape* shape, const float* centroids
                                 void* index_buf, size_t index_bytes, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of scratch workspace for pqhsa_append_tokens (0 if invalid). */
+size_t pqhsa_append_workspace_bytes(const pqhsa_shape* shape);
+
+/*
+ * Add tokens [n_indexed_b, new_n_indexed[b]) of each sequence to an uploaded
+ * index: the tokens held outside the index are added to it in batches
+ * (PQ-HSA page, section A, sixth paragraph; section C lists the update cost
+ * among the things to measure).
+ *
+ *   index_buf      an index written by pqhsa_upload_index (and possibly
+ *                  earlier appends) for `shape`; updated in place
+ *   k_cache, v_cache, block_table   as in pqhsa_decode_step; the new tokens'
+ *                  keys and values must be in the cache
+ *   new_n_indexed  int32 [B] device; new_n_indexed[b] >= the index's current
+ *                  n_indexed[b] and <= max_context
+ *   max_new        host bound on new_n_indexed[b] - n_indexed[b] over b
+ *                  (sizes the grid; tokens beyond it are not encoded)
+ *   list_ids       int32 [B][Hkv][max_context], the token-order list ids the
+ *                  index was uploaded from; entries of the new tokens are
+ *                  written, all indexed entries are read
+ *   codes          uint8 [B][Hkv][max_context][16], likewise
+ *
+ * For each new token t of (b, h), with K_t its key from the cache:
+ *   list_t   = argmin_c ||K_t - C_c||^2                  (lowest c on ties)
+ *   code_t,m = argmin_j ||(K_t - C[list_t])^(m) - B_m[j]||^2  (lowest j on ties)
+ * in fp32 (the residual IVF-PQ encoder matching the decode step's key model;
+ * the pages print no encoder).  The index is then regrouped by cluster over
+ * all indexed tokens (token order kept inside a cluster) and every cluster
+ * mean becomes (n_old * mean + sum of the new members' V) / n_new.  Finally
+ * the index's n_indexed becomes new_n_indexed.  Asynchronous on `stream`.
+ */
+pqhsa_status pqhsa_append_tokens(const pqhsa_shape* shape, void* index_buf,
+                                 const uint16_t* k_cache, const uint16_t* v_cache,
+                                 const int32_t* block_table, const int32_t* new_n_indexed,
+                                 int32_t max_new, int32_t* list_ids, uint8_t* codes,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Copy the count of dropped (out-of-range list id) tokens of an uploaded
  * index to *dropped.  Synchronises `stream`; meant for tests and tooling. */
 pqhsa_status pqhsa_index_dropped(const pqhsa_shape* shape, const void* index_buf,

@@ -12,6 +12,8 @@ import torch
 from . import _lib
 from ._lib import (  # noqa: F401
     EXPORTS,
+    append_tokens,
+    append_workspace_bytes,
     NUM_STAGES,
     VARIANT_DEFAULT,
     VARIANT_DENSE,
@@ -67,6 +69,17 @@ class PQHSADecoder:
         upload_index(self.shape, centroids, codebooks, list_ids, codes, n_indexed, v_cache,
                      block_table, self.index, ws, stream)
         self._upload_ws = ws          # keep alive until the stream has used it
+
+    def append(self, k_cache, v_cache, block_table, new_n_indexed, max_new, list_ids, codes,
+               stream=None):
+        """Add tokens [n_indexed, new_n_indexed) of each sequence to the index:
+        their list ids and codes are written into the token-order `list_ids`
+        and `codes` (the arrays the index was uploaded from)."""
+        ws = torch.empty(max(append_workspace_bytes(self.shape), 1), dtype=torch.uint8,
+                         device=self.device)
+        append_tokens(self.shape, self.index, k_cache, v_cache, block_table, new_n_indexed,
+                      max_new, list_ids, codes, ws, stream)
+        self._append_ws = ws          # keep alive until the stream has used it
 
     def step(self, q, k_cache, v_cache, block_table, context_lens, out=None, selected=False,
              lse=False, stream=None, staged=False):

@@ -54,7 +54,8 @@ EXPORTS = [
     "pqhsa_index_bytes", "pqhsa_upload_workspace_bytes", "pqhsa_workspace_bytes",
     "pqhsa_max_selected", "pqhsa_upload_index", "pqhsa_index_dropped", "pqhsa_decode_step",
     "pqhsa_dense_decode_step", "pqhsa_decode_step_profiled", "pqhsa_workspace_layout",
-    "pqhsa_index_layout_of", "pqhsa_status_string",
+    "pqhsa_index_layout_of", "pqhsa_status_string", "pqhsa_append_workspace_bytes",
+    "pqhsa_append_tokens",
 ]
 
 _lib = None
@@ -84,6 +85,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        [S, P, P, P, P, P, P, P, P, P, P, SZ, ctypes.c_int, P,
                                         ctypes.POINTER(ctypes.c_int32), P]),
         "pqhsa_workspace_layout": (ctypes.c_int, [S, ctypes.c_int, ctypes.POINTER(WsLayout)]),
+        "pqhsa_append_workspace_bytes": (SZ, [S]),
+        "pqhsa_append_tokens": (ctypes.c_int, [S, P, P, P, P, P, ctypes.c_int32, P, P, P, SZ, P]),
         "pqhsa_index_layout_of": (ctypes.c_int, [S, ctypes.POINTER(IndexLayout)]),
         "pqhsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
@@ -254,6 +257,25 @@ def decode_step_profiled(shape: Shape, index_buf, q, k_cache, v_cache, block_tab
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), int(variant), arr,
         ctypes.byref(nk), _stream(stream)))
     return nk.value
+
+
+def append_workspace_bytes(shape: Shape) -> int:
+    return load().pqhsa_append_workspace_bytes(ctypes.byref(shape))
+
+
+def append_tokens(shape: Shape, index_buf, k_cache, v_cache, block_table, new_n_indexed,
+                  max_new: int, list_ids, codes, workspace, stream=None):
+    """pqhsa_append_tokens: encode tokens [n_indexed, new_n_indexed) of each
+    sequence into `list_ids`/`codes` (token order) and update the index."""
+    B, Hkv, cap = shape.batch, shape.num_kv_heads, shape.max_context
+    _check("pqhsa_append_tokens", load().pqhsa_append_tokens(
+        ctypes.byref(shape), _ptr(index_buf, "index_buf", torch.uint8),
+        _ptr(k_cache, "k_cache", torch.int16), _ptr(v_cache, "v_cache", torch.int16),
+        _ptr(block_table, "block_table", torch.int32),
+        _ptr(new_n_indexed, "new_n_indexed", torch.int32, B), int(max_new),
+        _ptr(list_ids, "list_ids", torch.int32, B * Hkv * cap),
+        _ptr(codes, "codes", torch.uint8, B * Hkv * cap * 16),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
 
 
 # ------------------------------------------------------------------ HIP events

@@ -274,6 +274,23 @@ pqhsa_status run_step(const pqhsa_shape* shape, const void* index_buf, const uin
   return PQHSA_OK;
 }
 
+struct AppendWs {
+  size_t old_off, shift, codes, pos, list, total;
+};
+
+AppendWs append_ws(const Dims& d) {
+  const size_t BH = (size_t)d.B * d.Hkv;
+  AppendWs w;
+  size_t o = 0;
+  w.old_off = o; o = align_up(o + BH * (d.L + 1) * sizeof(int32_t));
+  w.shift = o;   o = align_up(o + BH * (d.L + 1) * sizeof(int32_t));
+  w.codes = o;   o = align_up(o + BH * d.cap * kM);
+  w.pos = o;     o = align_up(o + BH * d.cap * sizeof(int32_t));
+  w.list = o;    o = align_up(o + BH * d.cap * sizeof(int32_t));
+  w.total = o;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -331,6 +348,62 @@ pqhsa_status pqhsa_upload_index(const pqhsa_shape* shape, const float* centroids
                                       hipMemcpyDeviceToDevice, stream)));
   PQHSA_TRY(hip_status(hipMemsetAsync(a.ix.dropped, 0, sizeof(unsigned long long), stream)));
   return hip_status(launch_upload(a, stream));
+}
+
+size_t pqhsa_append_workspace_bytes(const pqhsa_shape* shape) {
+  if (validate(shape, false) != PQHSA_OK) return 0;
+  return append_ws(make_dims(shape, false)).total;
+}
+
+pqhsa_status pqhsa_append_tokens(const pqhsa_shape* shape, void* index_buf,
+                                 const uint16_t* k_cache, const uint16_t* v_cache,
+                                 const int32_t* block_table, const int32_t* new_n_indexed,
+                                 int32_t max_new, int32_t* list_ids, uint8_t* codes,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  PQHSA_TRY(validate(shape, false));
+  if (!index_buf || !k_cache || !v_cache || !block_table || !new_n_indexed || !list_ids ||
+      !codes || !workspace || max_new < 0)
+    return PQHSA_ERR_INVALID_ARG;
+  const Dims d = make_dims(shape, false);
+  if (max_new > d.cap) return PQHSA_ERR_INVALID_ARG;
+  const AppendWs lw = append_ws(d);
+  if (workspace_bytes < lw.total) return PQHSA_ERR_BUFFER_TOO_SMALL;
+  const size_t BH = (size_t)d.B * d.Hkv;
+  char* ws = static_cast<char*>(workspace);
+  AppendArgs aa;
+  memset(&aa, 0, sizeof(aa));
+  aa.d = d;
+  aa.ix = index_ptrs(d, index_buf);
+  aa.kc = k_cache;
+  aa.vc = v_cache;
+  aa.table = block_table;
+  aa.new_n_indexed = new_n_indexed;
+  aa.list_ids = list_ids;
+  aa.codes = codes;
+  aa.old_off = reinterpret_cast<int32_t*>(ws + lw.old_off);
+  aa.shift = reinterpret_cast<int32_t*>(ws + lw.shift);
+  aa.snap_codes = reinterpret_cast<uint8_t*>(ws + lw.codes);
+  aa.snap_pos = reinterpret_cast<int32_t*>(ws + lw.pos);
+  aa.snap_list = reinterpret_cast<int32_t*>(ws + lw.list);
+  // 1. encode the new tokens (reads the index's current n_indexed)
+  PQHSA_TRY(hip_status(launch_append_encode(aa, max_new, stream)));
+  // 2. snapshot the cluster offsets and the cluster-major arrays
+  PQHSA_TRY(hip_status(hipMemcpyAsync(ws + lw.old_off, aa.ix.list_off,
+                                      BH * (d.L + 1) * sizeof(int32_t), hipMemcpyDeviceToDevice,
+                                      stream)));
+  PQHSA_TRY(hip_status(hipMemcpyAsync(ws + lw.codes, aa.ix.codes, BH * d.cap * kM,
+                                      hipMemcpyDeviceToDevice, stream)));
+  PQHSA_TRY(hip_status(hipMemcpyAsync(ws + lw.pos, aa.ix.pos, BH * d.cap * sizeof(int32_t),
+                                      hipMemcpyDeviceToDevice, stream)));
+  PQHSA_TRY(hip_status(hipMemcpyAsync(ws + lw.list, aa.ix.ent_list, BH * d.cap * sizeof(int32_t),
+                                      hipMemcpyDeviceToDevice, stream)));
+  // 3. new offsets, old entries moved, new entries placed
+  PQHSA_TRY(hip_status(launch_append_regroup(aa, stream)));
+  // 4. fold the new tokens' values into the cluster means
+  PQHSA_TRY(hip_status(launch_append_means(aa, stream)));
+  // 5. the index now covers the new tokens
+  return hip_status(hipMemcpyAsync(aa.ix.n_indexed, new_n_indexed, d.B * sizeof(int32_t),
+                                   hipMemcpyDeviceToDevice, stream));
 }
 
 pqhsa_status pqhsa_index_dropped(const pqhsa_shape* shape, const void* index_buf,

@@ -120,6 +120,22 @@ struct UploadArgs {
   int32_t* chunk_counts;     // [BH][chunks][L]
 };
 
+struct AppendArgs {
+  Dims d;
+  IndexPtrs ix;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int32_t* table;
+  const int32_t* new_n_indexed;  // [B]
+  int32_t* list_ids;             // [BH][cap] token order (written for the new tokens)
+  uint8_t* codes;                // [BH][cap][16] token order (written for the new tokens)
+  const int32_t* old_off;        // [BH][L+1] cluster offsets before the append
+  int32_t* shift;                // [BH][L+1] new tokens in clusters before c
+  const uint8_t* snap_codes;     // [BH][cap][16] index arrays before the append
+  const int32_t* snap_pos;       // [BH][cap]
+  const int32_t* snap_list;      // [BH][cap]
+};
+
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -462,6 +478,10 @@ inline hipError_t launch_kernel(void (*kernel)(A), dim3 grid, dim3 block, size_t
 }
 
 hipError_t launch_upload(const UploadArgs& a, hipStream_t st);
+hipError_t launch_upload_regroup(const UploadArgs& a, hipStream_t st);
+hipError_t launch_append_encode(const AppendArgs& a, int max_new, hipStream_t st);
+hipError_t launch_append_means(const AppendArgs& a, hipStream_t st);
+hipError_t launch_append_regroup(const AppendArgs& a, hipStream_t st);
 hipError_t launch_tables(const StepArgs& a, const Launch& l);
 hipError_t launch_scan(const StepArgs& a, const Launch& l);
 hipError_t launch_collect(const StepArgs& a, const Launch& l);

@@ -178,7 +178,9 @@ __global__ __launch_bounds__(256) void k_upload_means(UploadArgs a) {
   }
 }
 
-hipError_t launch_upload(const UploadArgs& a, hipStream_t st) {
+// Counting sort of the token-order list ids and codes into the cluster-major
+// index (no means).
+hipError_t launch_upload_regroup(const UploadArgs& a, hipStream_t st) {
   const Dims& d = a.d;
   const int BH = d.B * d.Hkv;
   hipLaunchKernelGGL(k_upload_count, dim3(BH, d.upload_chunks), dim3(256),
@@ -186,6 +188,14 @@ hipError_t launch_upload(const UploadArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_upload_offsets, dim3(BH), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(k_upload_scatter, dim3(BH, d.upload_chunks), dim3(64),
                      d.L * sizeof(int32_t), st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_upload(const UploadArgs& a, hipStream_t st) {
+  const Dims& d = a.d;
+  const int BH = d.B * d.Hkv;
+  hipError_t e = launch_upload_regroup(a, st);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_upload_means, dim3(BH, (d.L + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
