@@ -10,6 +10,7 @@ from .gen import (  # noqa: F401
     StepInputs,
     f32_to_bf16_bits,
     bf16_bits_to_f32,
+    make_query_stream,
     make_step_inputs,
     page_layout,
     to_paged,

@@ -265,3 +265,44 @@ def to_paged(rows_bits: np.ndarray, context_lens, block_table: np.ndarray, num_p
         blk = blk.reshape(Hkv, n, page_size, D).transpose(1, 2, 0, 3)
         cache[block_table[b, :n]] = blk
     return cache
+
+
+def make_query_stream(workload_id: int, batch: int, num_q_heads: int, n_steps: int, *,
+                      n_topics: int = 4, p_stay: float = 0.8, spread: float = 1.0,
+                      jitter: float = 0.05, separate_search: bool = True):
+    """Seeded queries of consecutive decode steps, with repeats to reuse.
+
+    Recipe per (sequence b, query head hq), rng = default_rng([workload_id, b, hq, 11]):
+      topic centres  Z  = spread * N(0,1) of shape (n_topics, 128)
+      attention offsets Zq = spread * N(0,1) of shape (n_topics, 128)
+      topic of step 0 uniform in [0, n_topics); each later step keeps the
+      previous topic with probability p_stay, else draws it uniformly
+      search vector  q_search[t] = bf16( Z[topic_t] + jitter * N(0,1)^128 )
+      attention query q[t] = bf16( Zq[topic_t] + jitter * N(0,1)^128 ) when
+      separate_search, else q_search[t]
+    Returns (q_bits, qs_bits) of shape (n_steps, B, Hq, 128) uint16 and
+    topics (n_steps, B, Hq) int32.
+    """
+    q = np.zeros((n_steps, batch, num_q_heads, HEAD_DIM), np.uint16)
+    qs = np.zeros_like(q)
+    topics = np.zeros((n_steps, batch, num_q_heads), np.int32)
+    for b in range(batch):
+        for hq in range(num_q_heads):
+            rng = np.random.default_rng([workload_id, b, hq, 11])
+            Z = np.float32(spread) * rng.standard_normal((n_topics, HEAD_DIM), dtype=np.float32)
+            Zq = np.float32(spread) * rng.standard_normal((n_topics, HEAD_DIM), dtype=np.float32)
+            stay = rng.random(n_steps)
+            draw = rng.integers(0, n_topics, n_steps)
+            noise_s = rng.standard_normal((n_steps, HEAD_DIM), dtype=np.float32)
+            noise_q = rng.standard_normal((n_steps, HEAD_DIM), dtype=np.float32)
+            t = int(draw[0])
+            for i in range(n_steps):
+                if i > 0 and stay[i] >= p_stay:
+                    t = int(draw[i])
+                topics[i, b, hq] = t
+                qs[i, b, hq] = f32_to_bf16_bits(Z[t] + np.float32(jitter) * noise_s[i])
+                if separate_search:
+                    q[i, b, hq] = f32_to_bf16_bits(Zq[t] + np.float32(jitter) * noise_q[i])
+                else:
+                    q[i, b, hq] = qs[i, b, hq]
+    return q, qs, topics
