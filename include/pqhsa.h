@@ -296,6 +296,85 @@ typedef struct pqhsa_index_layout {
 } pqhsa_index_layout;
 pqhsa_status pqhsa_index_layout_of(const pqhsa_shape* shape, pqhsa_index_layout* out);
 
+/*
+ * ------------------------------------------------------------------ query reuse
+ * Dense decode attention that reuses the prefix numerator and denominator of a
+ * close earlier query (the quant_prune_distill post on query reuse, opening
+ * paragraph and sections "Important practical considerations" and
+ * "Experiments"): O = (N_P + N_S) / (D_P + D_S), where the prefix terms come
+ * from the earlier query's stored state and only the suffix is computed.
+ *
+ * Every query head of every sequence keeps a ring of `window` entries (1 to
+ * 8192; the post searches the last 1024 tokens), one per step: the step's
+ * search vector (bf16, 128 values), the state its attention produced (base-2
+ * maximum m, sum l and unnormalised acc[128], fp32) and the context length T_j
+ * it was computed at.  At context length T, head (b, hq):
+ *   eligible  = entries with 1 <= T_j <= T and T - T_j < window
+ *   d2_j      = sum_i (q_search[b][hq][i] - search_j[i])^2, fp32 from bf16
+ *   choice    = the eligible entry with the smallest d2, then the larger T_j,
+ *               then the lower slot
+ *   reuse     when a choice exists and d2 <= max_dist2
+ *   O         = attention of q[b][hq] over [T_j, T) merged with the entry's
+ *               state (reuse), or over [0, T) (no reuse)
+ * and the step's state is written to slot (count mod window) of the head's
+ * ring, with T_j = T, replacing the oldest entry.  (Comparing the pre-RoPE
+ * query vectors, one ring per query head, the window counted in steps, the
+ * squared distance and the tie order are readings where the post is silent:
+ * it names keys where it compares queries and gives no threshold.)
+ *
+ * Arguments as in pqhsa_dense_decode_step, plus:
+ *   window        ring slots per query head, 1..8192
+ *   max_dist2     reuse threshold on the squared distance (a negative value
+ *                 never reuses; NaN is invalid)
+ *   q_search      uint16 (bf16) [B][Hq][128] pre-RoPE vectors compared across
+ *                 steps (may equal q)
+ *   reuse_buf     device buffer of pqhsa_reuse_buffer_bytes(shape, window)
+ *                 bytes, owned by the caller and kept across steps; zero-filled
+ *                 or cleared with pqhsa_reuse_clear before its first step
+ *   reused_slot   int32 [B][Hq] optional: slot reused, -1 when none
+ *   min_dist2     float [B][Hq] optional: smallest eligible d2 (inf if none)
+ *   workspace     pqhsa_reuse_workspace_bytes(shape, window) bytes of scratch
+ * Steps on one reuse_buf must be ordered (same stream or synchronised); the
+ * step runs three kernels: search, split-K attention, merge and insert.
+ * Errors: PQHSA_ERR_INVALID_ARG for a NULL required pointer, a window out of
+ * range or a NaN threshold; PQHSA_ERR_BUFFER_TOO_SMALL for short buffers;
+ * shape errors as in pqhsa_dense_decode_step.
+ */
+size_t pqhsa_reuse_buffer_bytes(const pqhsa_shape* shape, int32_t window);
+size_t pqhsa_reuse_workspace_bytes(const pqhsa_shape* shape, int32_t window);
+
+/* Byte offsets of the rings inside reuse_buf: search [B*Hq][window][128] bf16,
+ * states [B*Hq][window][132] fp32 (m, l, 0, 0, acc[128]), context
+ * [B*Hq][window] int32 (T_j, 0 = empty) and count [B*Hq] int32. */
+typedef struct pqhsa_reuse_layout {
+  size_t search, states, context, count, total;
+} pqhsa_reuse_layout;
+pqhsa_status pqhsa_reuse_layout_of(const pqhsa_shape* shape, int32_t window,
+                                   pqhsa_reuse_layout* out);
+
+/* Empty the rings of sequences [seq_begin, seq_end) (for a new request in
+ * those batch slots).  Asynchronous on `stream`. */
+pqhsa_status pqhsa_reuse_clear(const pqhsa_shape* shape, int32_t window, void* reuse_buf,
+                               size_t reuse_bytes, int32_t seq_begin, int32_t seq_end,
+                               hipStream_t stream);
+
+pqhsa_status pqhsa_reuse_decode_step(const pqhsa_shape* shape, int32_t window, float max_dist2,
+                                     const uint16_t* q, const uint16_t* q_search,
+                                     const uint16_t* k_cache, const uint16_t* v_cache,
+                                     const int32_t* block_table, const int32_t* context_lens,
+                                     void* reuse_buf, size_t reuse_bytes, float* out, float* lse,
+                                     int32_t* reused_slot, float* min_dist2, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/* pqhsa_reuse_decode_step with its three kernels timed: events holds 6 events
+ * created by the caller, kernel i stamps events[2i] and events[2i+1]. */
+pqhsa_status pqhsa_reuse_decode_step_profiled(
+    const pqhsa_shape* shape, int32_t window, float max_dist2, const uint16_t* q,
+    const uint16_t* q_search, const uint16_t* k_cache, const uint16_t* v_cache,
+    const int32_t* block_table, const int32_t* context_lens, void* reuse_buf, size_t reuse_bytes,
+    float* out, float* lse, int32_t* reused_slot, float* min_dist2, void* workspace,
+    size_t workspace_bytes, hipEvent_t* events, int32_t* n_kernels, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* pqhsa_status_string(pqhsa_status status);
 

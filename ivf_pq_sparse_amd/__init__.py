@@ -21,6 +21,8 @@ from ._lib import (  # noqa: F401
     STAGE_NAMES,
     HipEvent,
     PQHSAError,
+    REUSE_KERNELS,
+    ReuseLayout,
     Shape,
     decode_step,
     decode_step_profiled,
@@ -31,6 +33,11 @@ from ._lib import (  # noqa: F401
     load,
     make_shape,
     max_selected,
+    reuse_buffer_bytes,
+    reuse_clear,
+    reuse_decode_step,
+    reuse_layout,
+    reuse_workspace_bytes,
     status_string,
     upload_index,
     upload_workspace_bytes,
@@ -124,3 +131,52 @@ class PQHSADecoder:
         dense_decode_step(s, q, k_cache, v_cache, block_table, context_lens, out,
                           self.dense_workspace(), lse=ls, stream=stream)
         return out, ls
+
+
+class ReuseDecoder:
+    """Dense decode attention with query reuse: owns the per-head query rings
+    (kept across steps) and the step's workspace."""
+
+    def __init__(self, shape: Shape, window: int = 1024, max_dist2: float = 1.0,
+                 device="cuda"):
+        load()
+        self.shape, self.window, self.max_dist2, self.device = shape, int(window), max_dist2, device
+        nb = reuse_buffer_bytes(shape, window)
+        if nb == 0:
+            raise PQHSAError("pqhsa_reuse_buffer_bytes", 1)
+        self.rings = torch.zeros(nb, dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(reuse_workspace_bytes(shape, window), dtype=torch.uint8,
+                                     device=device)
+        self.layout = reuse_layout(shape, window)
+
+    def clear(self, seq_begin: int = 0, seq_end=None, stream=None):
+        reuse_clear(self.shape, self.window, self.rings, seq_begin, seq_end, stream=stream)
+
+    def step(self, q, q_search, k_cache, v_cache, block_table, context_lens, out=None,
+             lse=False, report=False, events=None, stream=None):
+        """One step; returns (out, lse or None, reused slot or None, min d2 or None)."""
+        s = self.shape
+        BQ = (s.batch, s.num_q_heads)
+        if out is None:
+            out = torch.empty(*BQ, 128, dtype=torch.float32, device=self.device)
+        ls = torch.empty(*BQ, dtype=torch.float32, device=self.device) if lse else None
+        slot = torch.empty(*BQ, dtype=torch.int32, device=self.device) if report else None
+        d2 = torch.empty(*BQ, dtype=torch.float32, device=self.device) if report else None
+        reuse_decode_step(s, self.window, self.max_dist2, q, q_search, k_cache, v_cache,
+                          block_table, context_lens, self.rings, out, self.workspace, lse=ls,
+                          reused_slot=slot, min_dist2=d2, events=events, stream=stream)
+        return out, ls, slot, d2
+
+    def ring(self, name: str):
+        """A view of one ring array: "search" (int16 bf16 bits), "states"
+        (float32 [.., 132]), "context" or "count" (int32)."""
+        s, W = self.shape, self.window
+        BQ = s.batch * s.num_q_heads
+        off = getattr(self.layout, name)
+        if name == "search":
+            return self.rings[off:off + BQ * W * 256].view(torch.int16).view(s.batch, s.num_q_heads, W, 128)
+        if name == "states":
+            return self.rings[off:off + BQ * W * 528].view(torch.float32).view(s.batch, s.num_q_heads, W, 132)
+        if name == "context":
+            return self.rings[off:off + BQ * W * 4].view(torch.int32).view(s.batch, s.num_q_heads, W)
+        return self.rings[off:off + BQ * 4].view(torch.int32).view(s.batch, s.num_q_heads)

@@ -45,6 +45,10 @@ class WsLayout(ctypes.Structure):
         (n, ctypes.c_int32) for n in ("n_exact_splits", "n_bg_splits", "n_parts")]
 
 
+class ReuseLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("search", "states", "context", "count", "total")]
+
+
 class IndexLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "centroids", "codebooks", "list_off", "codes", "pos", "means", "n_indexed", "dropped")]
@@ -55,7 +59,9 @@ EXPORTS = [
     "pqhsa_max_selected", "pqhsa_upload_index", "pqhsa_index_dropped", "pqhsa_decode_step",
     "pqhsa_dense_decode_step", "pqhsa_decode_step_profiled", "pqhsa_workspace_layout",
     "pqhsa_index_layout_of", "pqhsa_status_string", "pqhsa_append_workspace_bytes",
-    "pqhsa_append_tokens",
+    "pqhsa_append_tokens", "pqhsa_reuse_buffer_bytes", "pqhsa_reuse_workspace_bytes",
+    "pqhsa_reuse_layout_of", "pqhsa_reuse_clear", "pqhsa_reuse_decode_step",
+    "pqhsa_reuse_decode_step_profiled",
 ]
 
 _lib = None
@@ -88,6 +94,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "pqhsa_append_workspace_bytes": (SZ, [S]),
         "pqhsa_append_tokens": (ctypes.c_int, [S, P, P, P, P, P, ctypes.c_int32, P, P, P, SZ, P]),
         "pqhsa_index_layout_of": (ctypes.c_int, [S, ctypes.POINTER(IndexLayout)]),
+        "pqhsa_reuse_buffer_bytes": (SZ, [S, I32]),
+        "pqhsa_reuse_workspace_bytes": (SZ, [S, I32]),
+        "pqhsa_reuse_layout_of": (ctypes.c_int, [S, I32, ctypes.POINTER(ReuseLayout)]),
+        "pqhsa_reuse_clear": (ctypes.c_int, [S, I32, P, SZ, I32, I32, P]),
+        "pqhsa_reuse_decode_step": (ctypes.c_int, [S, I32, ctypes.c_float, P, P, P, P, P, P, P,
+                                                   SZ, P, P, P, P, P, SZ, P]),
+        "pqhsa_reuse_decode_step_profiled": (ctypes.c_int,
+                                             [S, I32, ctypes.c_float, P, P, P, P, P, P, P, SZ,
+                                              P, P, P, P, P, SZ, P,
+                                              ctypes.POINTER(ctypes.c_int32), P]),
         "pqhsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -276,6 +292,60 @@ def append_tokens(shape: Shape, index_buf, k_cache, v_cache, block_table, new_n_
         _ptr(list_ids, "list_ids", torch.int32, B * Hkv * cap),
         _ptr(codes, "codes", torch.uint8, B * Hkv * cap * 16),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+
+
+# ------------------------------------------------------------------ query reuse
+REUSE_KERNELS = ("search", "attend", "merge")
+
+
+def reuse_buffer_bytes(shape: Shape, window: int) -> int:
+    return load().pqhsa_reuse_buffer_bytes(ctypes.byref(shape), int(window))
+
+
+def reuse_workspace_bytes(shape: Shape, window: int) -> int:
+    return load().pqhsa_reuse_workspace_bytes(ctypes.byref(shape), int(window))
+
+
+def reuse_layout(shape: Shape, window: int) -> ReuseLayout:
+    out = ReuseLayout()
+    _check("pqhsa_reuse_layout_of", load().pqhsa_reuse_layout_of(
+        ctypes.byref(shape), int(window), ctypes.byref(out)))
+    return out
+
+
+def reuse_clear(shape: Shape, window: int, reuse_buf, seq_begin: int = 0, seq_end=None,
+                stream=None):
+    """Empty the query rings of sequences [seq_begin, seq_end)."""
+    seq_end = shape.batch if seq_end is None else seq_end
+    _check("pqhsa_reuse_clear", load().pqhsa_reuse_clear(
+        ctypes.byref(shape), int(window), _ptr(reuse_buf, "reuse_buf", torch.uint8),
+        reuse_buf.numel(), int(seq_begin), int(seq_end), _stream(stream)))
+
+
+def reuse_decode_step(shape: Shape, window: int, max_dist2: float, q, q_search, k_cache,
+                      v_cache, block_table, context_lens, reuse_buf, out, workspace, lse=None,
+                      reused_slot=None, min_dist2=None, events=None, stream=None) -> int:
+    """pqhsa_reuse_decode_step (or its profiled form when `events`, 6
+    HipEvents, is given).  Returns the number of kernels launched (3)."""
+    qp, kp, vp, tp, cp, op, lp = _step_ptrs(shape, q, k_cache, v_cache, block_table,
+                                            context_lens, out, lse)
+    BQ = shape.batch * shape.num_q_heads
+    args = [ctypes.byref(shape), int(window), float(max_dist2), qp,
+            _ptr(_bf16(q_search), "q_search", torch.int16, BQ * 128), kp, vp, tp, cp,
+            _ptr(reuse_buf, "reuse_buf", torch.uint8), reuse_buf.numel(), op, lp,
+            _ptr(reused_slot, "reused_slot", torch.int32, BQ, optional=True),
+            _ptr(min_dist2, "min_dist2", torch.float32, BQ, optional=True),
+            _ptr(workspace, "workspace", torch.uint8), workspace.numel()]
+    if events is None:
+        _check("pqhsa_reuse_decode_step", load().pqhsa_reuse_decode_step(*args, _stream(stream)))
+        return len(REUSE_KERNELS)
+    if len(events) < 2 * len(REUSE_KERNELS):
+        raise ValueError(f"reuse_decode_step needs {2 * len(REUSE_KERNELS)} events")
+    arr = (ctypes.c_void_p * len(events))(*[e.handle for e in events])
+    nk = ctypes.c_int32(0)
+    _check("pqhsa_reuse_decode_step_profiled", load().pqhsa_reuse_decode_step_profiled(
+        *args, arr, ctypes.byref(nk), _stream(stream)))
+    return nk.value
 
 
 # ------------------------------------------------------------------ HIP events

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["pqhsa_api.hip", "pqhsa_upload.hip", "pqhsa_step.hip", "pqhsa_attn.hip",
-           "pqhsa_fused.hip", "pqhsa_append.hip"]
+           "pqhsa_fused.hip", "pqhsa_append.hip", "pqhsa_reuse.hip"]
 LIB_NAME = "libpqhsa.so"
 ARCH = "gfx950"
 

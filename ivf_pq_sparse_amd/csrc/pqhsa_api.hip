@@ -291,6 +291,98 @@ AppendWs append_ws(const Dims& d) {
   return w;
 }
 
+// Query reuse: the rings (caller-owned, persistent across steps) and the
+// step's workspace (split-K partials plus one reused state per query head,
+// then the search candidates).
+struct ReuseLayout {
+  size_t qs, st, tj, cnt, total;
+};
+
+ReuseLayout reuse_layout(const Dims& d, int W) {
+  ReuseLayout l;
+  const size_t BQ = (size_t)d.B * d.Hq;
+  size_t o = 0;
+  l.qs = o;  o = align_up(o + BQ * W * kD * sizeof(uint16_t));
+  l.st = o;  o = align_up(o + BQ * W * kPart * sizeof(float));
+  l.tj = o;  o = align_up(o + BQ * W * sizeof(int32_t));
+  l.cnt = o; o = align_up(o + BQ * sizeof(int32_t));
+  l.total = o;
+  return l;
+}
+
+int reuse_slabs(int W) { return ceil_div(W, kReuseSlab); }
+
+Dims reuse_dims(const pqhsa_shape* s) {
+  Dims d = make_dims(s, true);
+  d.n_parts = d.n_exact_splits + 1;
+  return d;
+}
+
+struct ReuseWs {
+  size_t partials, cand, total;
+};
+
+ReuseWs reuse_ws(const Dims& d, int W) {
+  ReuseWs w;
+  size_t o = 0;
+  w.partials = o; o = align_up(o + (size_t)d.B * d.Hq * d.n_parts * kPart * sizeof(float));
+  w.cand = o;     o = align_up(o + (size_t)d.B * d.Hq * reuse_slabs(W) * sizeof(int4));
+  w.total = o;
+  return w;
+}
+
+bool reuse_window_ok(int W) { return W >= 1 && W <= kReuseMaxWindow; }
+
+ReusePtrs reuse_ptrs(const Dims& d, int W, void* buf) {
+  const ReuseLayout l = reuse_layout(d, W);
+  char* p = static_cast<char*>(buf);
+  ReusePtrs r;
+  memset(&r, 0, sizeof(r));
+  r.qs = reinterpret_cast<uint16_t*>(p + l.qs);
+  r.st = reinterpret_cast<float*>(p + l.st);
+  r.tj = reinterpret_cast<int32_t*>(p + l.tj);
+  r.cnt = reinterpret_cast<int32_t*>(p + l.cnt);
+  r.W = W;
+  r.S = reuse_slabs(W);
+  return r;
+}
+
+pqhsa_status run_reuse(const pqhsa_shape* shape, int32_t window, float max_dist2,
+                       const uint16_t* q, const uint16_t* q_search, const uint16_t* k_cache,
+                       const uint16_t* v_cache, const int32_t* block_table,
+                       const int32_t* context_lens, void* reuse_buf, size_t reuse_bytes,
+                       float* out, float* lse, int32_t* reused_slot, float* min_dist2,
+                       void* workspace, size_t ws_bytes, hipEvent_t* evs, int* n_kernels,
+                       hipStream_t stream) {
+  PQHSA_TRY(validate(shape, true));
+  if (!reuse_window_ok(window) || isnan(max_dist2)) return PQHSA_ERR_INVALID_ARG;
+  if (!q || !q_search || !k_cache || !v_cache || !block_table || !context_lens || !reuse_buf ||
+      !out || !workspace)
+    return PQHSA_ERR_INVALID_ARG;
+  const Dims d = reuse_dims(shape);
+  if (reuse_bytes < reuse_layout(d, window).total) return PQHSA_ERR_BUFFER_TOO_SMALL;
+  const ReuseWs lw = reuse_ws(d, window);
+  if (ws_bytes < lw.total) return PQHSA_ERR_BUFFER_TOO_SMALL;
+  char* ws = static_cast<char*>(workspace);
+  StepArgs a;
+  memset(&a, 0, sizeof(a));
+  a.d = d;
+  a.ws.partials = reinterpret_cast<float*>(ws + lw.partials);
+  a.ru = reuse_ptrs(d, window, reuse_buf);
+  a.ru.cand = reinterpret_cast<int4*>(ws + lw.cand);
+  a.ru.q_search = q_search;
+  a.ru.slot_out = reused_slot;
+  a.ru.d2_out = min_dist2;
+  a.ru.max_d2 = max_dist2;
+  a.q = q; a.kc = k_cache; a.vc = v_cache; a.table = block_table; a.ctx = context_lens;
+  a.out = out; a.lse = lse;
+  PQHSA_TRY(hip_status(launch_reuse_search(a, stage(evs, 0, stream))));
+  PQHSA_TRY(hip_status(launch_exact_reuse(a, stage(evs, 1, stream))));
+  PQHSA_TRY(hip_status(launch_merge(a, stage(evs, 2, stream))));
+  if (n_kernels) *n_kernels = 3;
+  return PQHSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -490,6 +582,69 @@ pqhsa_status pqhsa_index_layout_of(const pqhsa_shape* shape, pqhsa_index_layout*
   out->codes = l.codes; out->pos = l.pos; out->means = l.means; out->n_indexed = l.n_indexed;
   out->dropped = l.dropped;
   return PQHSA_OK;
+}
+
+size_t pqhsa_reuse_buffer_bytes(const pqhsa_shape* shape, int32_t window) {
+  if (validate(shape, true) != PQHSA_OK || !reuse_window_ok(window)) return 0;
+  return reuse_layout(reuse_dims(shape), window).total;
+}
+
+size_t pqhsa_reuse_workspace_bytes(const pqhsa_shape* shape, int32_t window) {
+  if (validate(shape, true) != PQHSA_OK || !reuse_window_ok(window)) return 0;
+  return reuse_ws(reuse_dims(shape), window).total;
+}
+
+pqhsa_status pqhsa_reuse_layout_of(const pqhsa_shape* shape, int32_t window,
+                                   pqhsa_reuse_layout* out) {
+  PQHSA_TRY(validate(shape, true));
+  if (!reuse_window_ok(window) || !out) return PQHSA_ERR_INVALID_ARG;
+  const ReuseLayout l = reuse_layout(reuse_dims(shape), window);
+  out->search = l.qs; out->states = l.st; out->context = l.tj; out->count = l.cnt;
+  out->total = l.total;
+  return PQHSA_OK;
+}
+
+pqhsa_status pqhsa_reuse_clear(const pqhsa_shape* shape, int32_t window, void* reuse_buf,
+                               size_t reuse_bytes, int32_t seq_begin, int32_t seq_end,
+                               hipStream_t stream) {
+  PQHSA_TRY(validate(shape, true));
+  if (!reuse_window_ok(window) || !reuse_buf) return PQHSA_ERR_INVALID_ARG;
+  if (seq_begin < 0 || seq_end > shape->batch || seq_begin > seq_end) return PQHSA_ERR_INVALID_ARG;
+  const Dims d = reuse_dims(shape);
+  if (reuse_bytes < reuse_layout(d, window).total) return PQHSA_ERR_BUFFER_TOO_SMALL;
+  StepArgs a;
+  memset(&a, 0, sizeof(a));
+  a.d = d;
+  a.ru = reuse_ptrs(d, window, reuse_buf);
+  return hip_status(launch_reuse_clear(a, seq_begin, seq_end, stream));
+}
+
+pqhsa_status pqhsa_reuse_decode_step(const pqhsa_shape* shape, int32_t window, float max_dist2,
+                                     const uint16_t* q, const uint16_t* q_search,
+                                     const uint16_t* k_cache, const uint16_t* v_cache,
+                                     const int32_t* block_table, const int32_t* context_lens,
+                                     void* reuse_buf, size_t reuse_bytes, float* out, float* lse,
+                                     int32_t* reused_slot, float* min_dist2, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  return run_reuse(shape, window, max_dist2, q, q_search, k_cache, v_cache, block_table,
+                   context_lens, reuse_buf, reuse_bytes, out, lse, reused_slot, min_dist2,
+                   workspace, workspace_bytes, nullptr, nullptr, stream);
+}
+
+pqhsa_status pqhsa_reuse_decode_step_profiled(
+    const pqhsa_shape* shape, int32_t window, float max_dist2, const uint16_t* q,
+    const uint16_t* q_search, const uint16_t* k_cache, const uint16_t* v_cache,
+    const int32_t* block_table, const int32_t* context_lens, void* reuse_buf, size_t reuse_bytes,
+    float* out, float* lse, int32_t* reused_slot, float* min_dist2, void* workspace,
+    size_t workspace_bytes, hipEvent_t* events, int32_t* n_kernels, hipStream_t stream) {
+  if (!events) return PQHSA_ERR_INVALID_ARG;
+  int nk = 0;
+  const pqhsa_status st =
+      run_reuse(shape, window, max_dist2, q, q_search, k_cache, v_cache, block_table,
+                context_lens, reuse_buf, reuse_bytes, out, lse, reused_slot, min_dist2,
+                workspace, workspace_bytes, events, &nk, stream);
+  if (n_kernels) *n_kernels = nk;
+  return st;
 }
 
 const char* pqhsa_status_string(pqhsa_status status) {

@@ -10,7 +10,10 @@
 // post on query reuse, over all partials.  Dense and sparse modes share the
 // split-K kernel, as the activation/KV-sparsity crossover article (rit.work
 // blog, section "Why one method gives different speed-ups") requires of an
-// honest baseline.
+// honest baseline.  The same split-K kernel also serves query reuse: each
+// query head starts at the context length of the earlier query whose prefix
+// state it reuses (0 when it reuses none), and the reused state joins the
+// merge as one more partial.
 //
 // Split-K block: 256 threads = 16 row groups of 16 lanes (one DPP row each).
 // The block first stages the cache offsets of up to 256 rows in LDS (row list
@@ -32,7 +35,56 @@ struct AttendLds {
   long long row_off[kPhaseRows];
   float ml[4][G][2];
   float acc[4][G][kD];
+  int rstart[G];   // query reuse: first position computed for head g
+  int rslot[G];    // query reuse: reused slot of head g, or -1
 };
+
+// Where the rows of a split-K block come from.
+enum RowSource {
+  kRowsIndex = 0,   // the step's exact-row list (sink, selected, recent)
+  kRowsDense = 1,   // the whole context [0, T)
+  kRowsReuse = 2    // [start_g, T) per query head g, after the reuse decision
+};
+
+// Reuse decision of the G query heads of (b, h): the best candidate over the
+// head's search slabs, ordered by (distance, larger T_j, lower slot); the
+// head reuses it when its distance is within the threshold.  Fills
+// sh.rstart / sh.rslot; with `report`, also writes the optional outputs.
+template <int G>
+__device__ void reuse_decide(const StepArgs& a, int b, int h, bool report, AttendLds<G>& sh) {
+  const ReusePtrs& r = a.ru;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int g = wave; g < G; g += 4) {
+    const int bq = b * a.d.Hq + h * G + g;
+    uint32_t khi = 0xffffffffu, klo = 0xffffffffu;
+    int sl = -1;
+    if (lane < r.S) {
+      const int4 c = r.cand[(size_t)bq * r.S + lane];
+      khi = (uint32_t)c.x;
+      klo = ~(uint32_t)c.y;
+      sl = c.z;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint32_t ohi = __shfl_xor(khi, o), olo = __shfl_xor(klo, o);
+      const int os = __shfl_xor(sl, o);
+      const bool take = ohi < khi || (ohi == khi && (olo < klo || (olo == klo &&
+                                                                   (uint32_t)os < (uint32_t)sl)));
+      if (take) { khi = ohi; klo = olo; sl = os; }
+    }
+    if (lane == 0) {
+      const float d2 = __uint_as_float(khi);
+      const bool reuse = sl >= 0 && d2 <= r.max_d2;
+      sh.rslot[g] = reuse ? sl : -1;
+      sh.rstart[g] = reuse ? (int)~klo : 0;
+      if (report) {
+        if (r.slot_out) r.slot_out[bq] = reuse ? sl : -1;
+        if (r.d2_out) r.d2_out[bq] = sl >= 0 ? d2 : INFINITY;
+      }
+    }
+  }
+  __syncthreads();
+}
 
 // Merge the per-wave states held in LDS (ml, acc) and store one partial per
 // query head at `slot`.
@@ -60,20 +112,54 @@ __device__ void block_merge_store(AttendLds<G>& sh, float* part_base, int n_part
   }
 }
 
-// Split-K exact attention for one (b, h, split): rows [r0, r1) of either the
-// index-list row array (DENSE = false) or the whole context (DENSE = true).
-template <int G, bool DENSE>
+// Split-K exact attention for one (b, h, split): its share of the rows of the
+// source SRC (see RowSource).  With kRowsReuse, split 0 also places each
+// head's reused state (or an empty one) in the partial after the splits'.
+template <int G, int SRC>
 __device__ void exact_block(const StepArgs& a, int bh, int split, AttendLds<G>& sh) {
   const Dims& d = a.d;
   const int b = bh / d.Hkv, h = bh % d.Hkv;
   const int l16 = threadIdx.x & 15;
   const int rg = threadIdx.x >> 4;
-  int n_rows;
-  if constexpr (DENSE) n_rows = min(max(a.ctx[b], 0), d.cap);
-  else n_rows = min(max(a.ws.n_rows[bh], 0), d.cap);
+  int n_rows, base = 0;
+  int s0[G] = {};
+  if constexpr (SRC == kRowsIndex) {
+    n_rows = min(max(a.ws.n_rows[bh], 0), d.cap);
+  } else {
+    const int T = min(max(a.ctx[b], 0), d.cap);
+    if constexpr (SRC == kRowsReuse) {
+      reuse_decide<G>(a, b, h, split == 0, sh);
+      base = T;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        s0[g] = min(sh.rstart[g], T);
+        base = min(base, s0[g]);
+      }
+      if (split == 0) {
+        const ReusePtrs& r = a.ru;
+        float* pb = a.ws.partials + ((size_t)b * d.Hq + h * G) * d.n_parts * kPart;
+        for (int i = threadIdx.x; i < G * kPart; i += blockDim.x) {
+          const int g = i / kPart, e = i % kPart;
+          const int sl = sh.rslot[g];
+          float v = e == 0 ? -INFINITY : 0.0f;
+          if (sl >= 0) v = r.st[((size_t)(b * d.Hq + h * G + g) * r.W + sl) * kPart + e];
+          pb[((size_t)g * d.n_parts + d.n_exact_splits) * kPart + e] = v;
+        }
+      }
+    }
+    n_rows = T - base;
+  }
   const int chunk = (n_rows + d.n_exact_splits - 1) / d.n_exact_splits;
-  const int r0 = min(n_rows, split * chunk);
-  const int r1 = min(n_rows, r0 + chunk);
+  const int r0 = base + min(n_rows, split * chunk);
+  const int r1 = base + min(n_rows, split * chunk + chunk);
+  // heads that take row `p` (all of them unless some reuse a prefix)
+  auto act = [&](int p) -> uint32_t {
+    if constexpr (SRC != kRowsReuse) return 0xffu;
+    uint32_t m = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) m |= (uint32_t)(p >= s0[g]) << g;
+    return m;
+  };
 
   float qv[G][8];
   {
@@ -102,7 +188,8 @@ __device__ void exact_block(const StepArgs& a, int bh, int split, AttendLds<G>& 
   for (int ph = r0; ph < r1; ph += kPhaseRows) {
     const int n = min(kPhaseRows, r1 - ph);
     if ((int)threadIdx.x < n) {
-      const int p = DENSE ? ph + (int)threadIdx.x : min(max(rows[ph + threadIdx.x], 0), d.cap - 1);
+      const int p = SRC != kRowsIndex ? ph + (int)threadIdx.x
+                                      : min(max(rows[ph + threadIdx.x], 0), d.cap - 1);
       int page = tab[p >> 4];
       page = min(max(page, 0), d.num_pages - 1);
       sh.row_off[threadIdx.x] =
@@ -134,8 +221,8 @@ __device__ void exact_block(const StepArgs& a, int bh, int split, AttendLds<G>& 
         nk1 = *reinterpret_cast<const uint4*>(kc + o);
         nv1 = *reinterpret_cast<const uint4*>(vc + o);
       }
-      attend_row<G>(st, qv, k0, v0);
-      if (j + 16 < n) attend_row<G>(st, qv, k1, v1);
+      attend_row<G>(st, qv, k0, v0, act(ph + j));
+      if (j + 16 < n) attend_row<G>(st, qv, k1, v1, act(ph + j + 16));
       k0 = nk0; v0 = nv0; k1 = nk1; v1 = nv1;
       j = jn;
     }
@@ -242,7 +329,7 @@ __device__ void background_block(const StepArgs& a, int bh, int split, AttendLds
 }
 
 // One launch for both: blocks [0, BH*n_exact) do split-K, the rest background.
-template <int G, bool DENSE>
+template <int G, int SRC>
 __global__ __launch_bounds__(256) void k_attend(StepArgs a) {
   __shared__ AttendLds<G> sh;
   const int BH = a.d.B * a.d.Hkv;
@@ -251,8 +338,8 @@ __global__ __launch_bounds__(256) void k_attend(StepArgs a) {
   int bh, sub;
   if (blk < n_exact_blocks) {
     xcd_map(blk, BH, a.d.n_exact_splits, &bh, &sub);
-    exact_block<G, DENSE>(a, bh, sub, sh);
-  } else if constexpr (!DENSE) {
+    exact_block<G, SRC>(a, bh, sub, sh);
+  } else if constexpr (SRC == kRowsIndex) {
     xcd_map(blk - n_exact_blocks, BH, a.d.n_bg_splits, &bh, &sub);
     background_block<G>(a, bh, sub, sh);
   }
@@ -318,6 +405,26 @@ __global__ __launch_bounds__(256) void k_merge(StepArgs a) {
     const float tot = sum + half1[dim];
     a.out[(size_t)bq * kD + dim] = L > 0.0f ? tot / L : 0.0f;
     if (dim == 0 && a.lse) a.lse[bq] = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+    if (a.ru.st) {
+      // query reuse: this step's state goes into the head's ring
+      const int w = (int)((uint32_t)a.ru.cnt[bq] % (uint32_t)a.ru.W);
+      float* dst = a.ru.st + ((size_t)bq * a.ru.W + w) * kPart;
+      dst[4 + dim] = tot;
+      if (dim == 0) { dst[0] = M; dst[1] = L; dst[2] = 0.0f; dst[3] = 0.0f; }
+      if (dim < kD / 8)
+        *reinterpret_cast<uint4*>(a.ru.qs + ((size_t)bq * a.ru.W + w) * kD + dim * 8) =
+            *reinterpret_cast<const uint4*>(a.ru.q_search + (size_t)bq * kD + dim * 8);
+    }
+  }
+  if (a.ru.st) {
+    __syncthreads();   // every thread has read the count
+    if (tid == 0) {
+      const int c = a.ru.cnt[bq];
+      const int b = bh / a.d.Hkv;
+      a.ru.tj[(size_t)bq * a.ru.W + (uint32_t)c % (uint32_t)a.ru.W] =
+          min(max(a.ctx[b], 0), a.d.cap);
+      a.ru.cnt[bq] = c + 1;
+    }
   }
 }
 
@@ -325,9 +432,16 @@ template <int G>
 static hipError_t attend_g(const StepArgs& a, bool dense, const Launch& l) {
   const int BH = a.d.B * a.d.Hkv;
   if (dense)
-    return launch_kernel(k_attend<G, true>, dim3(BH * a.d.n_exact_splits), dim3(256), 0, l, a);
-  return launch_kernel(k_attend<G, false>, dim3(BH * (a.d.n_exact_splits + a.d.n_bg_splits)),
+    return launch_kernel(k_attend<G, kRowsDense>, dim3(BH * a.d.n_exact_splits), dim3(256), 0, l,
+                         a);
+  return launch_kernel(k_attend<G, kRowsIndex>, dim3(BH * (a.d.n_exact_splits + a.d.n_bg_splits)),
                        dim3(256), 0, l, a);
+}
+
+template <int G>
+static hipError_t attend_reuse_g(const StepArgs& a, const Launch& l) {
+  const int BH = a.d.B * a.d.Hkv;
+  return launch_kernel(k_attend<G, kRowsReuse>, dim3(BH * a.d.n_exact_splits), dim3(256), 0, l, a);
 }
 
 #define PQHSA_G_DISPATCH2(fn, ...)                  \
@@ -341,6 +455,10 @@ static hipError_t attend_g(const StepArgs& a, bool dense, const Launch& l) {
 
 hipError_t launch_exact_and_background(const StepArgs& a, bool dense, const Launch& l) {
   PQHSA_G_DISPATCH2(attend_g, a, dense, l)
+}
+
+hipError_t launch_exact_reuse(const StepArgs& a, const Launch& l) {
+  PQHSA_G_DISPATCH2(attend_reuse_g, a, l)
 }
 
 hipError_t launch_merge(const StepArgs& a, const Launch& l) {

@@ -35,6 +35,8 @@ constexpr int kBgBatch = 4;             // clusters whose loads a background wav
 constexpr int kUploadChunk = 4096;      // tokens per counting-sort chunk
 constexpr int kMaxFusedP = 64;          // fused step: at most this many blocks per (b, h)
 constexpr int kFusedWselMax = 1024;     // fused step: clusters per block x G held in LDS
+constexpr int kReuseSlab = 128;         // ring slots per search block
+constexpr int kReuseMaxWindow = 64 * kReuseSlab;   // slabs of a ring fit one wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFixScale = 1099511627776.0f;   // 2^40: fixed-point unit of selected weights
 constexpr float kFixInv = 1.0f / 1099511627776.0f;
@@ -94,10 +96,27 @@ struct WsPtrs {
   float* fpart;        // [BH][G][kMaxFusedP][132] one partial per block and query head
 };
 
+// Query reuse: the per-(sequence, query head) rings of earlier queries and
+// the step's inputs and outputs that belong to reuse only.
+struct ReusePtrs {
+  uint16_t* qs;               // [B*Hq][W][128] bf16 search vectors
+  float* st;                  // [B*Hq][W][132] states: m (base 2), l, pad, pad, acc[128]
+  int32_t* tj;                // [B*Hq][W] context length at insertion, 0 = empty slot
+  int32_t* cnt;               // [B*Hq] entries inserted so far
+  int4* cand;                 // [B*Hq][S] best entry of each slab: (d2 bits, T_j, slot, 0)
+  const uint16_t* q_search;   // [B][Hq][128] bf16
+  int32_t* slot_out;          // [B][Hq] reused slot or -1 (optional)
+  float* d2_out;              // [B][Hq] smallest eligible squared distance (optional)
+  int W;                      // slots per ring (the search window in tokens)
+  int S;                      // search slabs per ring, ceil(W / kReuseSlab)
+  float max_d2;               // reuse when the smallest distance is <= this
+};
+
 struct StepArgs {
   Dims d;
   IndexPtrs ix;
   WsPtrs ws;
+  ReusePtrs ru;
   const uint16_t* q;
   const uint16_t* kc;
   const uint16_t* vc;
@@ -427,9 +446,12 @@ struct AttnState {
   float m[G], l[G], acc[G][8];
 };
 
+// One K/V row into the online softmax of the G query heads; head g takes the
+// row only when bit g of `act` is set (the dot products run for all heads, so
+// every lane of the row's DPP row takes part in the reductions).
 template <int G>
 __device__ __forceinline__ void attend_row(AttnState<G>& st, const float (&qv)[G][8], uint4 kw,
-                                           uint4 vw) {
+                                           uint4 vw, uint32_t act = 0xffu) {
   const float kf[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
                        bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
   const float vf[8] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y),
@@ -440,13 +462,15 @@ __device__ __forceinline__ void attend_row(AttnState<G>& st, const float (&qv)[G
 #pragma unroll
     for (int i = 1; i < 8; ++i) s = fmaf(qv[g][i], kf[i], s);
     s = row16_sum(s);
-    const float mn = fmaxf(st.m[g], s);
-    const float al = exp2f(st.m[g] - mn);
-    const float p = exp2f(s - mn);
-    st.l[g] = fmaf(st.l[g], al, p);
+    if (act & (1u << g)) {
+      const float mn = fmaxf(st.m[g], s);
+      const float al = exp2f(st.m[g] - mn);
+      const float p = exp2f(s - mn);
+      st.l[g] = fmaf(st.l[g], al, p);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st.acc[g][i] = fmaf(st.acc[g][i], al, p * vf[i]);
-    st.m[g] = mn;
+      for (int i = 0; i < 8; ++i) st.acc[g][i] = fmaf(st.acc[g][i], al, p * vf[i]);
+      st.m[g] = mn;
+    }
   }
 }
 
@@ -488,6 +512,9 @@ hipError_t launch_collect(const StepArgs& a, const Launch& l);
 hipError_t launch_select(const StepArgs& a, const Launch& l);
 hipError_t launch_exact_and_background(const StepArgs& a, bool dense, const Launch& l);
 hipError_t launch_merge(const StepArgs& a, const Launch& l);
+hipError_t launch_exact_reuse(const StepArgs& a, const Launch& l);
+hipError_t launch_reuse_search(const StepArgs& a, const Launch& l);
+hipError_t launch_reuse_clear(const StepArgs& a, int seq_begin, int seq_end, hipStream_t st);
 // Fused step: blocks per (b, h) that fit co-resident on the device (0 when the
 // fused kernel cannot run this shape), and its launch.
 int fused_blocks_per_head(const Dims& d);

@@ -161,3 +161,47 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         pq.dense_decode_step(s, torch.zeros(512, dtype=torch.int16), None, None, None, None,
                              None, None)
+
+
+def test_reuse_sizes_window_limits_and_validation(lib, shape):
+    import ivf_pq_sparse_amd as pq
+    # rings: 32 heads x 1024 slots x (256 B search + 528 B state + 4 B context)
+    # plus the counts: about 5 % of the layer's 512 MiB K/V cache at 128K
+    nb = pq.reuse_buffer_bytes(shape, 1024)
+    assert nb >= 32 * 1024 * (256 + 528 + 4) + 32 * 4
+    assert 0.04 < nb / (131072 * 8 * 128 * 2 * 2) < 0.06
+    lay = pq.reuse_layout(shape, 1024)
+    assert lay.search == 0 and lay.states >= 32 * 1024 * 256
+    assert lay.context >= lay.states + 32 * 1024 * 528 and lay.count > lay.context
+    assert lay.total == nb
+    assert pq.reuse_workspace_bytes(shape, 1024) > 0
+    for w in (0, -1, 8193):
+        assert pq.reuse_buffer_bytes(shape, w) == 0
+        assert pq.reuse_workspace_bytes(shape, w) == 0
+    assert pq.reuse_buffer_bytes(shape, 8192) > 0
+    fake = ctypes.c_void_p(0x1000)
+    S = ctypes.byref(shape)
+    need = lib.pqhsa_reuse_buffer_bytes(S, 64)
+    wneed = lib.pqhsa_reuse_workspace_bytes(S, 64)
+    ok_args = [fake] * 7
+    def call(window=64, thr=1.0, ptrs=None, nb=need, wb=wneed, buf=fake):
+        p = ok_args if ptrs is None else ptrs
+        return lib.pqhsa_reuse_decode_step(S, window, thr, p[0], p[1], p[2], p[3], p[4], p[5],
+                                           buf, nb, p[6], None, None, None, fake, wb, None)
+    for i in range(7):
+        ptrs = list(ok_args)
+        ptrs[i] = None
+        assert call(ptrs=ptrs) == INVALID
+    assert call(buf=None) == INVALID
+    assert call(window=0) == INVALID and call(window=9000) == INVALID
+    assert call(thr=float("nan")) == INVALID
+    assert call(nb=need - 1) == TOO_SMALL
+    assert call(wb=wneed - 1) == TOO_SMALL
+    assert lib.pqhsa_reuse_decode_step_profiled(S, 64, 1.0, *ok_args[:6], fake, need, fake,
+                                                None, None, None, fake, wneed, None, None,
+                                                None) == INVALID
+    assert lib.pqhsa_reuse_clear(S, 64, fake, need, 0, 2, None) == INVALID
+    assert lib.pqhsa_reuse_clear(S, 64, fake, need, -1, 1, None) == INVALID
+    assert lib.pqhsa_reuse_clear(S, 64, fake, need - 1, 0, 1, None) == TOO_SMALL
+    assert lib.pqhsa_reuse_clear(S, 64, None, need, 0, 1, None) == INVALID
+    assert lib.pqhsa_reuse_layout_of(S, 64, None) == INVALID
