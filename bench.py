@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain device copy of known size (for counter scaling)")
-    p.add_argument("--sweep", choices=["configs", "budget", "context", "append"],
+    p.add_argument("--sweep", choices=["configs", "budget", "context", "append", "reuse"],
                    help="print a markdown table of a sweep instead of the JSON line")
     p.add_argument("--summarize-profile", nargs=4, metavar=("TRACE", "FETCH", "WRITE", "OUT"),
                    help="write the markdown summary of three rocprofv3 output folders and exit")
@@ -222,7 +222,7 @@ class Rig:
     permutation and index, together larger than the 256 MB Infinity Cache)
     and timed loops over them."""
 
-    def __init__(self, inp, n_layers=0, exact_only=0, max_bytes=60e9):
+    def __init__(self, inp, n_layers=0, exact_only=0, max_bytes=60e9, with_index=True):
         import torch
 
         import ivf_pq_sparse_amd as pq
@@ -233,7 +233,8 @@ class Rig:
         kv_bytes = 2 * tens["k_cache"].numel() * 2
         self.kv_bytes = kv_bytes
         n = n_layers or max(2, int(np.ceil(2.5 * 256e6 / (kv_bytes / 17.6 + 1))))
-        n = min(n, max(2, int(max_bytes // (kv_bytes + pq.index_bytes(self.shape)))))
+        ix_bytes = pq.index_bytes(self.shape) if with_index else 0
+        n = min(n, max(2, int(max_bytes // (kv_bytes + ix_bytes))))
         self.n_layers = n
         self.layers = []
         g = torch.Generator(device="cpu").manual_seed(1234)
@@ -247,15 +248,22 @@ class Rig:
             bt = tens["block_table"].clone()
             valid = bt >= 0
             bt[valid] = perm[bt[valid].long()].to(torch.int32)
-            dec = pq.PQHSADecoder(self.shape)
-            dec.upload(tens["centroids"], tens["codebooks"], tens["list_ids"], tens["codes"],
-                       tens["n_indexed"], vc, bt)
+            dec = None
+            if with_index:
+                dec = pq.PQHSADecoder(self.shape)
+                dec.upload(tens["centroids"], tens["codebooks"], tens["list_ids"], tens["codes"],
+                           tens["n_indexed"], vc, bt)
             self.layers.append(dict(kc=kc, vc=vc, bt=bt, dec=dec))
         torch.cuda.synchronize()
         del tens["k_cache"], tens["v_cache"]
         self.q, self.ctx = tens["q"], tens["context_lens"]
-        self.ws = self.layers[0]["dec"].workspace
-        self.dense_ws = self.layers[0]["dec"].dense_workspace()
+        if with_index:
+            self.ws = self.layers[0]["dec"].workspace
+            self.dense_ws = self.layers[0]["dec"].dense_workspace()
+        else:
+            self.ws = None
+            self.dense_ws = torch.empty(pq.workspace_bytes(self.shape, True), dtype=torch.uint8,
+                                        device="cuda")
         self.out = torch.empty(self.shape.batch, self.shape.num_q_heads, 128,
                                dtype=torch.float32, device="cuda")
 
@@ -284,6 +292,88 @@ class Rig:
         e1.synchronize()
         torch.cuda.synchronize()
         return e0.elapsed_ms(e1) / steps * 1e3
+
+
+def reuse_sweep(steps, warmup, window=1024):
+    """Query reuse at the 128K Llama-3.1-8B layer shape: every layer copy keeps
+    its own rings; step i runs all copies at context T0 + i with search
+    vectors that repeat with period `dist` (exact repeats, so every head
+    reuses the entry of `dist` steps earlier: a suffix of `dist` tokens).
+    "none" sets a negative threshold (search, then full attention); dense is
+    the plain split-K step on the same copies."""
+    import torch
+
+    import ivf_pq_sparse_amd as pq
+    from pqhsa_synth import f32_to_bf16_bits, make_step_inputs
+    n_total = 1100 + warmup + steps + 16
+    T_end = 131072
+    inp = make_step_inputs(2, context_lens=[T_end], num_lists=8, n_tail=0)
+    rig = Rig(inp, with_index=False)
+    shape, B, Hq = rig.shape, rig.shape.batch, rig.shape.num_q_heads
+    rng = np.random.default_rng(5)
+    topics = rng.standard_normal((1024, B, Hq, 128)).astype(np.float32)
+    qbits = torch.from_numpy(f32_to_bf16_bits(topics).view(np.int16)).cuda()
+    decs = [pq.ReuseDecoder(shape, window=window, max_dist2=0.5) for _ in range(rig.n_layers)]
+    out = torch.empty(B, Hq, 128, dtype=torch.float32, device="cuda")
+    ctxs = [torch.tensor([T_end - n_total + i] * B, dtype=torch.int32, device="cuda")
+            for i in range(n_total)]
+    slot = torch.empty(B, Hq, dtype=torch.int32, device="cuda")
+    d2 = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+    evs = [pq.HipEvent() for _ in range(6)]
+    stream = torch.cuda.current_stream()
+    dense_us = rig.timed(True, steps * rig.n_layers // 4, warmup)
+    print(f"K/V copies: {rig.n_layers}; window {window}; dense split-K step {dense_us:.1f} µs")
+    print()
+    print("| reuse distance (tokens) | heads reusing | wall µs per layer-step | kernel µs | "
+          "dense µs | speed-up (kernels) | search µs | attend µs | merge µs |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for dist in (1, 8, 64, 256, 1000, "none"):
+        period = 1000 if dist == "none" else dist
+        for d in decs:
+            d.clear()
+            d.max_dist2 = -1.0 if dist == "none" else 0.5
+
+        def run(i, layer, events=None):
+            d = decs[layer]
+            L_ = rig.layers[layer]
+            q = qbits[i % period]
+            d.step(q, q, L_["kc"], L_["vc"], L_["bt"], ctxs[i], out=out, events=events)
+
+        n_warm = period + warmup
+        for i in range(n_warm):
+            for layer in range(rig.n_layers):
+                run(i, layer)
+        torch.cuda.synchronize()
+        e0, e1 = pq.HipEvent(), pq.HipEvent()
+        e0.record(stream)
+        for i in range(n_warm, n_warm + steps):
+            for layer in range(rig.n_layers):
+                run(i, layer)
+        e1.record(stream)
+        e1.synchronize()
+        us = e0.elapsed_ms(e1) * 1e3 / (steps * rig.n_layers)
+        # kernel split on further steps, and the share of heads reusing
+        ks = np.zeros(3)
+        n_prof = 8
+        for j in range(n_prof + 1):     # j = 0: untimed first use of the events
+            i = n_warm + steps + j
+            layer = j % rig.n_layers
+            L_ = rig.layers[layer]
+            q = qbits[i % period]
+            pq.reuse_decode_step(shape, window, decs[layer].max_dist2, q, q, L_["kc"], L_["vc"],
+                                 L_["bt"], ctxs[i], decs[layer].rings, out, decs[layer].workspace,
+                                 reused_slot=slot, min_dist2=d2, events=evs)
+            for r in range(layer + 1, rig.n_layers):
+                run(i, r)
+            evs[5].synchronize()
+            if j:
+                ks += [evs[2 * k].elapsed_ms(evs[2 * k + 1]) * 1e3 for k in range(3)]
+        ks /= n_prof
+        frac = float((slot >= 0).float().mean())
+        kus = float(ks.sum())
+        print(f"| {dist} | {frac * 100:.0f} % | {us:.1f} | {kus:.1f} | {dense_us:.1f} | "
+              f"{dense_us / kus:.2f} | {ks[0]:.1f} | {ks[1]:.1f} | {ks[2]:.1f} |", flush=True)
+        log(f"reuse distance {dist}: {us:.1f} µs per layer-step (dense {dense_us:.1f})")
 
 
 def sweep(name, steps, warmup):
@@ -406,6 +496,8 @@ def sweep(name, steps, warmup):
             log(f"{what} {ntok}: {us:.1f} µs")
             del dec, tens
             torch.cuda.empty_cache()
+    elif name == "reuse":
+        reuse_sweep(steps, warmup)
     else:
         raise SystemExit(f"unknown sweep {name}")
 

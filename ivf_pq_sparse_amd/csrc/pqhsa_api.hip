@@ -319,7 +319,7 @@ Dims reuse_dims(const pqhsa_shape* s) {
 }
 
 struct ReuseWs {
-  size_t partials, cand, total;
+  size_t partials, cand, n_merge, total;
 };
 
 ReuseWs reuse_ws(const Dims& d, int W) {
@@ -327,6 +327,7 @@ ReuseWs reuse_ws(const Dims& d, int W) {
   size_t o = 0;
   w.partials = o; o = align_up(o + (size_t)d.B * d.Hq * d.n_parts * kPart * sizeof(float));
   w.cand = o;     o = align_up(o + (size_t)d.B * d.Hq * reuse_slabs(W) * sizeof(int4));
+  w.n_merge = o;  o = align_up(o + (size_t)d.B * d.Hkv * sizeof(int32_t));
   w.total = o;
   return w;
 }
@@ -368,6 +369,7 @@ pqhsa_status run_reuse(const pqhsa_shape* shape, int32_t window, float max_dist2
   memset(&a, 0, sizeof(a));
   a.d = d;
   a.ws.partials = reinterpret_cast<float*>(ws + lw.partials);
+  a.ws.n_rows = reinterpret_cast<int32_t*>(ws + lw.n_merge);
   a.ru = reuse_ptrs(d, window, reuse_buf);
   a.ru.cand = reinterpret_cast<int4*>(ws + lw.cand);
   a.ru.q_search = q_search;

@@ -113,15 +113,19 @@ __device__ void block_merge_store(AttendLds<G>& sh, float* part_base, int n_part
 }
 
 // Split-K exact attention for one (b, h, split): its share of the rows of the
-// source SRC (see RowSource).  With kRowsReuse, split 0 also places each
-// head's reused state (or an empty one) in the partial after the splits'.
+// source SRC (see RowSource).  With kRowsReuse the rows [base, T) (base the
+// smallest start of the G heads) go to splits of equal size (at least
+// kReuseMinRows rows), and only the n_act splits that have rows run; split 0
+// also places each head's
+// reused state (or an empty one) in partial n_act and records n_act + 1, the
+// number of partials the merge reads.
 template <int G, int SRC>
 __device__ void exact_block(const StepArgs& a, int bh, int split, AttendLds<G>& sh) {
   const Dims& d = a.d;
   const int b = bh / d.Hkv, h = bh % d.Hkv;
   const int l16 = threadIdx.x & 15;
   const int rg = threadIdx.x >> 4;
-  int n_rows, base = 0;
+  int n_rows, base = 0, split_rows = 0;
   int s0[G] = {};
   if constexpr (SRC == kRowsIndex) {
     n_rows = min(max(a.ws.n_rows[bh], 0), d.cap);
@@ -135,6 +139,12 @@ __device__ void exact_block(const StepArgs& a, int bh, int split, AttendLds<G>& 
         s0[g] = min(sh.rstart[g], T);
         base = min(base, s0[g]);
       }
+      // short suffixes still spread over several blocks: at least
+      // kReuseMinRows rows per split, at most the grid's splits
+      const int n_sfx = T - base;
+      const int rows = max(kReuseMinRows, (n_sfx + d.n_exact_splits - 1) / d.n_exact_splits);
+      const int n_act = (n_sfx + rows - 1) / rows;
+      split_rows = rows;
       if (split == 0) {
         const ReusePtrs& r = a.ru;
         float* pb = a.ws.partials + ((size_t)b * d.Hq + h * G) * d.n_parts * kPart;
@@ -143,15 +153,23 @@ __device__ void exact_block(const StepArgs& a, int bh, int split, AttendLds<G>& 
           const int sl = sh.rslot[g];
           float v = e == 0 ? -INFINITY : 0.0f;
           if (sl >= 0) v = r.st[((size_t)(b * d.Hq + h * G + g) * r.W + sl) * kPart + e];
-          pb[((size_t)g * d.n_parts + d.n_exact_splits) * kPart + e] = v;
+          pb[((size_t)g * d.n_parts + n_act) * kPart + e] = v;
         }
+        if (threadIdx.x == 0) a.ws.n_rows[bh] = n_act + 1;
       }
+      if (split >= n_act) return;   // no rows for this split (uniform per block)
     }
     n_rows = T - base;
   }
-  const int chunk = (n_rows + d.n_exact_splits - 1) / d.n_exact_splits;
-  const int r0 = base + min(n_rows, split * chunk);
-  const int r1 = base + min(n_rows, split * chunk + chunk);
+  int r0, r1;
+  if constexpr (SRC == kRowsReuse) {
+    r0 = base + split * split_rows;
+    r1 = min(base + n_rows, r0 + split_rows);
+  } else {
+    const int chunk = (n_rows + d.n_exact_splits - 1) / d.n_exact_splits;
+    r0 = base + min(n_rows, split * chunk);
+    r1 = base + min(n_rows, split * chunk + chunk);
+  }
   // heads that take row `p` (all of them unless some reuse a prefix)
   auto act = [&](int p) -> uint32_t {
     if constexpr (SRC != kRowsReuse) return 0xffu;
@@ -352,13 +370,14 @@ __global__ __launch_bounds__(256) void k_attend(StepArgs a) {
 __global__ __launch_bounds__(256) void k_merge(StepArgs a) {
   extern __shared__ float mlds[];   // [np] weights, [np] sums, [128] second half's sums
   __shared__ float red[8];
-  const int np = a.d.n_parts;
   const int G = a.d.G;
   int bh, g;
   xcd_map(blockIdx.x, a.d.B * a.d.Hkv, G, &bh, &g);
+  // query reuse merges only the partials its attention wrote
+  const int np = a.ru.st ? min(max(a.ws.n_rows[bh], 1), a.d.n_parts) : a.d.n_parts;
   const int bq = (bh / a.d.Hkv) * a.d.Hq + (bh % a.d.Hkv) * G + g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* part = a.ws.partials + (size_t)bq * np * kPart;
+  const float* part = a.ws.partials + (size_t)bq * a.d.n_parts * kPart;
   float* wts = mlds;
   float* ls = mlds + np;
   float* half1 = mlds + 2 * np;

@@ -36,6 +36,7 @@ constexpr int kUploadChunk = 4096;      // tokens per counting-sort chunk
 constexpr int kMaxFusedP = 64;          // fused step: at most this many blocks per (b, h)
 constexpr int kFusedWselMax = 1024;     // fused step: clusters per block x G held in LDS
 constexpr int kReuseSlab = 128;         // ring slots per search block
+constexpr int kReuseMinRows = 64;       // query reuse: fewest rows per split-K block
 constexpr int kReuseMaxWindow = 64 * kReuseSlab;   // slabs of a ring fit one wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFixScale = 1099511627776.0f;   // 2^40: fixed-point unit of selected weights
@@ -87,7 +88,7 @@ struct WsPtrs {
   unsigned long long* wsel;  // [BH][L][G] selected entries' weights per cluster, fixed point 2^-40
                              // (written by the selection with plain stores)
   int32_t* rows;       // [BH][cap] exact rows as physical cache rows (page * 16 + slot)
-  int32_t* n_rows;     // [BH]
+  int32_t* n_rows;     // [BH] exact rows (query reuse: partials to merge)
   float* partials;     // [B][Hq][n_parts][132]
   // fused step only
   uint32_t* fsync;     // [BH][4] arrivals at the two per-head barriers, finished blocks
