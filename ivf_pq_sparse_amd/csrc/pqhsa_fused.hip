@@ -847,56 +847,50 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     }
   }
   __syncthreads();
-  // merge the wave's 4 row groups, then the waves through LDS
+  // Block merge: every row group's state goes to LDS; the weight of each
+  // (row group, head) against the head's max is computed once; then each
+  // thread sums one output (head, dim) over the row groups.
+  static_assert(NG == 32 && (size_t)NG * G * kD * sizeof(float) <= C::kUBytes, "row states");
+  float* accr = reinterpret_cast<float*>(dyn);           // [NG][G][128]
+  float* mlr = reinterpret_cast<float*>(hist);           // [NG][G][2]
+  float* fr = mlr + NG * G * 2;                          // [G][NG]
+  float* mlg = fr + G * NG;                              // [G][2] head max and sum
 #pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(st.m[g], o);
-      const float lo_ = __shfl_xor(st.l[g], o);
-      float M, a0, a1;
-      lse_factors(st.m[g], mo, &M, &a0, &a1);
-      st.l[g] = st.l[g] * a0 + lo_ * a1;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float ao = __shfl_xor(st.acc[g][i], o);
-        st.acc[g][i] = st.acc[g][i] * a0 + ao * a1;
-      }
-      st.m[g] = M;
+  for (int g = 0; g < G; ++g) {
+    if (l16 == 0) {
+      mlr[(rg * G + g) * 2] = st.m[g];
+      mlr[(rg * G + g) * 2 + 1] = st.l[g];
     }
+    float4* dst = reinterpret_cast<float4*>(accr + ((size_t)rg * G + g) * kD + l16 * 8);
+    dst[0] = make_float4(st.acc[g][0], st.acc[g][1], st.acc[g][2], st.acc[g][3]);
+    dst[1] = make_float4(st.acc[g][4], st.acc[g][5], st.acc[g][6], st.acc[g][7]);
   }
-  float* mlw = reinterpret_cast<float*>(dyn);           // [NW][G][2]
-  float* accw = mlw + NW * G * 2;                        // [NW][G][128]
-  if (lane < 16) {
+  __syncthreads();
+  if (tid < G * NG) {
+    // one 32-lane half wave per head
+    const int g = tid / NG, r = tid % NG;
+    const float m = mlr[(r * G + g) * 2];
+    float M = m;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (l16 == 0) {
-        mlw[(wave * G + g) * 2] = st.m[g];
-        mlw[(wave * G + g) * 2 + 1] = st.l[g];
-      }
+    for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    fr[g * NG + r] = f;
+    float L = f * mlr[(r * G + g) * 2 + 1];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) accw[(wave * G + g) * kD + l16 * 8 + i] = st.acc[g][i];
-    }
+    for (int o = 16; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+    if (r == 0) { mlg[g * 2] = M; mlg[g * 2 + 1] = L; }
   }
   __syncthreads();
   for (int idx = tid; idx < G * kD; idx += NT) {
     const int g = idx / kD, dim = idx % kD;
-    float M = -INFINITY;
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, mlw[(w * G + g) * 2]);
-    float L = 0.0f, A = 0.0f;
-    if (M != -INFINITY) {
-      for (int w = 0; w < NW; ++w) {
-        const float mw = mlw[(w * G + g) * 2];
-        const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-        L = fmaf(f, mlw[(w * G + g) * 2 + 1], L);
-        A = fmaf(f, accw[(w * G + g) * kD + dim], A);
-      }
-    }
+    float A = 0.0f;
+#pragma unroll 8
+    for (int r = 0; r < NG; ++r) A = fmaf(fr[g * NG + r], accr[((size_t)r * G + g) * kD + dim], A);
     float* out = a.ws.fpart + (((size_t)bh * G + g) * kMaxFusedP + sub) * kPart;
     st_dev(&out[4 + dim], A);
     if (dim == 0) {
-      st_dev(&out[0], M);
-      st_dev(&out[1], L);
+      st_dev(&out[0], mlg[g * 2]);
+      st_dev(&out[1], mlg[g * 2 + 1]);
     }
   }
   wait_mem();
@@ -911,42 +905,45 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
 
   // ======================================================= last block of the head
   // every (head, dim) thread loads its column of the P partials (a wave's
-  // loads of one partial are contiguous) while the first G*P threads stage
-  // the (m, l) pairs in LDS
+  // loads of one partial are contiguous) while one wave per head loads the
+  // (m, l) pairs and forms the weights of the partials against the head's max
   {
-    float* mlp = reinterpret_cast<float*>(hist);   // [G][P][2]
+    float* fp = reinterpret_cast<float*>(hist);     // [G][64] weights
+    float* mlh = fp + G * kMaxFusedP;               // [G][2] head max and sum
     constexpr int kOut = (G * kD + NT - 1) / NT;    // outputs per thread
     const float* pbase = a.ws.fpart + (size_t)bh * G * kMaxFusedP * kPart;
-    if (tid < G * P) {
-      const int g = tid / P, j = tid % P;
-      const float* pp = pbase + ((size_t)g * kMaxFusedP + j) * kPart;
-      mlp[tid * 2] = ld_dev(&pp[0]);
-      mlp[tid * 2 + 1] = ld_dev(&pp[1]);
-    }
-    for (int o = 0; o < kOut; ++o) {
+    float x[kMaxFusedP];
+    auto load_col = [&](int o) {
       // threads past the outputs load a valid column and discard it
       const int idx = min(tid + o * NT, G * kD - 1);
-      const int g = idx / kD, dim = idx % kD;
-      const float* col = pbase + (size_t)g * kMaxFusedP * kPart + 4 + dim;
-      float x[kMaxFusedP];
+      const float* col = pbase + (size_t)(idx / kD) * kMaxFusedP * kPart + 4 + idx % kD;
 #pragma unroll
       for (int j = 0; j < kMaxFusedP; ++j) x[j] = j < P ? ld_dev(&col[(size_t)j * kPart]) : 0.0f;
-      __syncthreads();
-      if (tid + o * NT < G * kD) {
-        float M = -INFINITY;
-        for (int j = 0; j < P; ++j) M = fmaxf(M, mlp[(g * P + j) * 2]);
-        float L = 0.0f, A = 0.0f;
-        if (M != -INFINITY) {
+    };
+    load_col(0);
+    for (int g = wave; g < G; g += NW) {
+      const float* pp = pbase + ((size_t)g * kMaxFusedP + lane) * kPart;
+      const float m = lane < P ? ld_dev(&pp[0]) : -INFINITY;
+      const float l = lane < P ? ld_dev(&pp[1]) : 0.0f;
+      const float M = wave_max_dpp(m);
+      const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+      fp[g * kMaxFusedP + lane] = f;
+      const float L = wave_sum_dpp(f * l);
+      if (lane == 0) { mlh[g * 2] = M; mlh[g * 2 + 1] = L; }
+    }
+    __syncthreads();
 #pragma unroll
-          for (int j = 0; j < kMaxFusedP; ++j) {
-            if (j < P) {
-              const float mj = mlp[(g * P + j) * 2];
-              const float f = (mj == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mj - M);
-              L = fmaf(f, mlp[(g * P + j) * 2 + 1], L);
-              A = fmaf(f, x[j], A);
-            }
-          }
-        }
+    for (int o = 0; o < kOut; ++o) {
+      if (o > 0) load_col(o);
+      const int idx = tid + o * NT;
+      if (idx < G * kD) {
+        const int g = idx / kD, dim = idx % kD;
+        const float* fg = fp + g * kMaxFusedP;
+        float A = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kMaxFusedP; ++j)
+          if (j < P) A = fmaf(fg[j], x[j], A);
+        const float M = mlh[g * 2], L = mlh[g * 2 + 1];
         const size_t bq = (size_t)b * d.Hq + h * G + g;
         a.out[bq * kD + dim] = L > 0.0f ? A / L : 0.0f;
         if (dim == 0 && a.lse)
