@@ -158,44 +158,55 @@ __device__ void block_scan2(int a, int b, int* oa, int* ob, int* ta, int* tb, in
   __syncthreads();
 }
 
-// One wave, over bins [lo, 4096) of a histogram in LDS (bin = top 12 bits of
-// the key): the bucket beta holding the k-th largest key counted from the top,
-// i.e. above(beta) < k <= above(beta) + hist[beta] with above(x) the count in
-// bins (x, 4096); k is first capped at the range's total.  Two levels: lane l
-// sums the 64 bins below 4096 - 64 l (lane 0 the highest; read in a rotated
-// order, free of bank conflicts), a wave scan and a ballot pick the lane whose
-// range crosses k, then the wave takes that range's 64 bins one per lane and
-// finds the bin the same way.  Writes beta (-1 if the capped k is 0),
-// above(beta) and the total to out[0..2].
-__device__ void wave_threshold(const uint32_t* hist, int lo, int k, int* out) {
-  const int lane = threadIdx.x & 63;
-  const int hi = kHistBins - 64 * lane;
+// The whole block, over bins [lo, 4096) of a histogram in LDS (bin = top 12
+// bits of the key): the bucket beta holding the k-th largest key counted from
+// the top, i.e. above(beta) < k <= above(beta) + hist[beta] with above(x) the
+// count in bins (x, 4096); k is first capped at the range's total.  Thread t
+// sums the 4096/NT bins below 4096 - t*4096/NT (thread 0 the highest); a
+// block scan of the sums in that order finds the one thread whose range
+// crosses k, which walks its bins.
+// Writes beta (-1 if the capped k is 0), above(beta) and the total to
+// out[0..2]; sh holds NT/64 ints.  Ends with a block barrier.
+template <int NT>
+__device__ void block_threshold(const uint32_t* hist, int lo, int k, int* out, int* sh) {
+  constexpr int PER = kHistBins / NT;
+  static_assert(PER * NT == kHistBins && PER % 4 == 0, "bins per thread");
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hi = kHistBins - PER * tid;   // this thread's bins are [hi - PER, hi)
+  uint32_t v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i += 4) {
+    const uint4 w = *reinterpret_cast<const uint4*>(hist + hi - PER + i);
+    v[i] = w.x; v[i + 1] = w.y; v[i + 2] = w.z; v[i + 3] = w.w;
+  }
   int s = 0;
-  if (hi > lo) {
-    // x stays within [hi - 64, hi) inside the table: loads need no guard
-#pragma unroll 16
-    for (int i = 0; i < 64; ++i) {
-      const int x = hi - 1 - ((i + lane) & 63);
-      const int v = (int)hist[x];
-      s += x >= lo ? v : 0;
-    }
-  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s += (hi - PER + i >= lo) ? (int)v[i] : 0;
   const int inc = wave_incl_scan(s);
-  const int tot = __builtin_amdgcn_readlane(inc, 63);
-  const int kk = min(k, tot);
-  int beta = -1, above = 0;
-  if (kk > 0) {
-    const int L = __ffsll((long long)__ballot(inc >= kk)) - 1;
-    const int before = __shfl(inc, L) - __shfl(s, L);
-    const int x = kHistBins - 64 * L - 1 - lane;
-    const int vx = (int)hist[x];
-    const int v = x >= lo ? vx : 0;
-    const int inc2 = wave_incl_scan(v);
-    const int l2 = __ffsll((long long)__ballot(before + inc2 >= kk)) - 1;
-    beta = kHistBins - 64 * L - 1 - l2;
-    above = before + __shfl(inc2, l2) - __shfl(v, l2);
+  if (lane == 63) sh[wave] = inc;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = sh[w];
+    before += w < wave ? t : 0;
+    tot += t;
   }
-  if (lane == 0) { out[0] = beta; out[1] = above; out[2] = tot; }
+  const int kk = min(k, tot);
+  const int x1 = before + inc, x0 = x1 - s;   // counts above and through this range
+  if (kk > 0 && x0 < kk && kk <= x1) {
+    int run = x0, beta = hi - PER;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      const int c = (hi - PER + i >= lo) ? (int)v[i] : 0;
+      if (run + c >= kk) { beta = hi - PER + i; break; }
+      run += c;
+    }
+    out[0] = beta; out[1] = run; out[2] = tot;
+  }
+  if (kk == 0 && tid == 0) { out[0] = -1; out[1] = 0; out[2] = tot; }
+  __syncthreads();
 }
 
 __device__ __forceinline__ unsigned long long tie_composite(unsigned long long rec) {
@@ -516,8 +527,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   // bins >= beta_b, so the head's threshold bucket is >= beta_b and the bins
   // below cannot matter.  Only bins >= beta_b go to the head's histogram
   // (fewer atomics on shared lines), and only those are read back.
-  if (wave == 0) wave_threshold(hist, 0, si.k, S.res);
-  __syncthreads();
+  block_threshold<NT>(hist, 0, si.k, S.res, S.sh);
   const int beta_b = S.res[0];   // -1: no candidate in this block, or k = 0
   // with fewer than k candidates of its own the block flushes every bin, and
   // the head's threshold may lie below its bins: it then reads them all
@@ -539,8 +549,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   if (beta_b >= 0) {
     for (int i = read_lo + tid; i < kHistBins; i += NT) hist[i] = ld_dev(&ghist[i]);
     __syncthreads();
-    if (wave == 0) wave_threshold(hist, read_lo, si.k, S.res);
-    __syncthreads();
+    block_threshold<NT>(hist, read_lo, si.k, S.res, S.sh);
     beta = S.res[0];
     __syncthreads();
   }
@@ -940,9 +949,9 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
         const int g = idx / kD, dim = idx % kD;
         const float* fg = fp + g * kMaxFusedP;
         float A = 0.0f;
+        // weights and loads are 0 for j >= P
 #pragma unroll
-        for (int j = 0; j < kMaxFusedP; ++j)
-          if (j < P) A = fmaf(fg[j], x[j], A);
+        for (int j = 0; j < kMaxFusedP; ++j) A = fmaf(fg[j], x[j], A);
         const float M = mlh[g * 2], L = mlh[g * 2 + 1];
         const size_t bq = (size_t)b * d.Hq + h * G + g;
         a.out[bq * kD + dim] = L > 0.0f ? A / L : 0.0f;
