@@ -62,9 +62,13 @@ struct FusedCfg {
   static constexpr int kItems = NG * kItemsPerGroup;   // attention items staged per phase
   static constexpr size_t kUBytes = (size_t)kM * kKsub * G * sizeof(float);   // LUT, then reuse
   static constexpr size_t kHBytes = (size_t)kHistBins * sizeof(uint32_t);
-  static constexpr size_t kWBytes = (size_t)kFusedWselMax * sizeof(unsigned long long);
-  static constexpr size_t kQBytes = (size_t)kFusedWselMax * sizeof(float);
-  static constexpr size_t kDyn = kUBytes + kHBytes + kWBytes + kQBytes;
+  // clusters x G per block whose per-cluster values live in LDS (smaller at
+  // G = 8, whose 128 KB LUT leaves less room)
+  static constexpr int kCG = G == 8 ? kFusedWselMax / 2 : kFusedWselMax;
+  static constexpr size_t kWBytes = (size_t)kCG * sizeof(unsigned long long);   // selected weights
+  static constexpr size_t kQBytes = (size_t)kCG * sizeof(float);                // cluster logits
+  static constexpr size_t kBBytes = (size_t)kCG * 2 * sizeof(float);            // cluster (max, sum)
+  static constexpr size_t kDyn = kUBytes + kHBytes + kWBytes + kQBytes + kBBytes;
   static constexpr int kTieCap = (int)(kUBytes / sizeof(unsigned long long));
   static_assert((size_t)NW * G * (2 + kD) * sizeof(float) <= kUBytes, "merge arrays");
   static_assert((size_t)kItems * sizeof(long long) + 4096 <= kHBytes, "item staging");
@@ -290,6 +294,8 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   uint32_t* hist = reinterpret_cast<uint32_t*>(dyn + C::kUBytes);
   unsigned long long* wsel = reinterpret_cast<unsigned long long*>(dyn + C::kUBytes + C::kHBytes);
   float* qcl = reinterpret_cast<float*>(dyn + C::kUBytes + C::kHBytes + C::kWBytes);   // [ncl][G]
+  // (max, sum of exp2) of every cluster of the block and query head: [ncl][G][2]
+  float* binl = reinterpret_cast<float*>(dyn + C::kUBytes + C::kHBytes + C::kWBytes + C::kQBytes);
 
   const Dims& d = a.d;
   const int P = d.fP;
@@ -309,7 +315,6 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   uint32_t* ghist = a.ws.hist + (size_t)bh * kHistBins;
   uint32_t* keys = a.ws.keys + (size_t)bh * d.cap;
   float* qcg = a.ws.qc + (size_t)bh * d.L * G;
-  float* bins = a.ws.bins + (size_t)bh * d.L * G * 2;
   const uint4* codes = reinterpret_cast<const uint4*>(a.ix.codes + (size_t)bh * d.cap * kM);
   const int32_t* pos = a.ix.pos + (size_t)bh * d.cap;
   const int32_t* ent_list = a.ix.ent_list + (size_t)bh * d.cap;
@@ -501,8 +506,8 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
         const float part = (mx[g] == -INFINITY) ? 0.0f : sm[g] * __builtin_amdgcn_exp2f(mx[g] - M);
         const float Ssum = wave_sum_dpp(part);
         if (lane == 0) {
-          bins[((size_t)c * G + g) * 2] = M;
-          bins[((size_t)c * G + g) * 2 + 1] = Ssum;
+          binl[((c - c0) * G + g) * 2] = M;
+          binl[((c - c0) * G + g) * 2 + 1] = Ssum;
         }
         mx[g] = -INFINITY;
         sm[g] = 0.0f;
@@ -562,7 +567,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     entry_logits_lds<G>(lut, q, cw, sv);
 #pragma unroll
     for (int g = 0; g < G; ++g)
-      w[g] = __builtin_amdgcn_exp2f(sv[g] - bins[((size_t)cl * G + g) * 2]);
+      w[g] = __builtin_amdgcn_exp2f(sv[g] - binl[((cl - c0) * G + g) * 2]);
   };
   // The block's entries in chunks of NT*16 (entry cb + u*NT + tid to thread
   // tid): count, one block scan, list the chosen entries in LDS (above ones
@@ -786,8 +791,8 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   long long* ioff = reinterpret_cast<long long*>(dyn + C::kUBytes + 4096);
   for (int i = tid; i < ncl * G; i += NT) {
     const int cl = c0 + i / G, g = i % G;
-    const float M = bins[((size_t)cl * G + g) * 2];
-    const float wb = bins[((size_t)cl * G + g) * 2 + 1] - (float)wsel[i] * kFixInv;
+    const float M = binl[((cl - c0) * G + g) * 2];
+    const float wb = binl[((cl - c0) * G + g) * 2 + 1] - (float)wsel[i] * kFixInv;
     sbg[i] = (wb > 0.0f && M != -INFINITY) ? M + log2f(wb) : -INFINITY;
   }
   // exact rows and background clusters as one item list through 16-lane groups
@@ -1062,6 +1067,16 @@ size_t fused_lds_bytes(int G) {
   return 0;
 }
 
+int fused_cluster_cap(int G) {
+  switch (G) {
+    case 1: return FusedCfg<1>::kCG;
+    case 2: return FusedCfg<2>::kCG;
+    case 4: return FusedCfg<4>::kCG;
+    case 8: return FusedCfg<8>::kCG;
+  }
+  return 0;
+}
+
 int fused_blocks_per_head(const Dims& d) {
   const FusedDeviceInfo* fi = device_info();
   if (!fi || fi->occ[g_index(d.G)] < 1) return 0;
@@ -1076,7 +1091,7 @@ int fused_blocks_per_head(const Dims& d) {
   if (p0 > by_work) p0 = by_work;
   if (p0 < 1) return 0;
   const int cpb = (int)((d.L + p0 - 1) / p0);
-  if ((long long)cpb * d.G > kFusedWselMax) return 0;
+  if ((long long)cpb * d.G > fused_cluster_cap(d.G)) return 0;
   // the selected-position bitmap of the last block lives in LDS
   const size_t lut_hist = (size_t)kM * kKsub * d.G * sizeof(float) + kHistBins * sizeof(uint32_t);
   if ((size_t)d.nwords * 4 > lut_hist) return 0;
