@@ -340,15 +340,11 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       }
     }
   };
-  // the wave's first round goes out before the tables are built
+  // the wave's first round goes out before the tables are built, after the
+  // tables' own loads (which need no index offsets)
   int c = c0 + wave;
   int e0 = 0, e1 = 0;
   FRound<G, PT> rb[2];
-  if (c < c1) {
-    e0 = entry_at(c);
-    e1 = max(e0, entry_at(c + 1));
-    issue(rb[0], e0, e1);
-  }
   {
     // LUT[m][j][g] = scale*log2e * q_g^(m) . B_m[j].  Every thread's codebook
     // rows are loaded at once (codeword j = tid % 256, subspaces tid / 256 +
@@ -373,9 +369,16 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       cen0 = *reinterpret_cast<const float4*>(cp);
       cen1 = *reinterpret_cast<const float4*>(cp + 4);
     }
+    uint4 qw = make_uint4(0, 0, 0, 0);
+    if (tid < G * kD / 8) qw = *reinterpret_cast<const uint4*>(qh + tid * 8);
+    if (c < c1) {
+      e0 = entry_at(c);
+      e1 = max(e0, entry_at(c + 1));
+      issue(rb[0], e0, e1);
+    }
     float* qsl = reinterpret_cast<float*>(hist);   // scaled q [G][128] until the QC pass
     if (tid < G * kD / 8) {
-      const uint4 w = *reinterpret_cast<const uint4*>(qh + tid * 8);
+      const uint4 w = qw;
       const float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                           bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
 #pragma unroll
