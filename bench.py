@@ -213,7 +213,7 @@ def kernel_of_stage(stage, G):
     """Kernel symbol (as rocprofv3 shortens it) that a stage launches."""
     return {"fused": f"k_fused<{G}>",
             "tables": f"k_tables<{G}>", "scan": f"k_scan<{G}>", "collect": f"k_collect<{G}>",
-            "select": f"k_select<{G}>", "attend": f"k_attend<{G},false>",
+            "select": f"k_select<{G}>", "attend": f"k_attend<{G},0>",
             "merge": "k_merge"}[stage]
 
 
