@@ -663,8 +663,54 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   auto tie_rec = [&](int i) -> unsigned long long {
     return cached ? tcache[i] : ld_dev(&ftie[tie_slot(i)]);
   };
-  if (r > 0 && cached)
-    for (int i = tid; i < n_tie; i += NT) tcache[i] = ld_dev(&ftie[tie_slot(i)]);
+  // The tie records into LDS, and with them this block's own tie records'
+  // clusters and weights (the histogram region is free until the background
+  // logits), so that placing the winners needs no global load.
+  constexpr int kOwnCap = (int)(C::kHBytes / ((1 + G) * sizeof(float)));
+  float* ownw = reinterpret_cast<float*>(hist);                  // [kOwnCap][G]
+  int* ownc = reinterpret_cast<int*>(ownw + (size_t)kOwnCap * G);   // [kOwnCap]
+  const int own0 = S.tpre[sub];
+  {
+    const int n_t = (r > 0 && cached) ? n_tie : 0;
+    const int n_o = r > 0 ? min(S.tpre[sub + 1] - own0, kOwnCap) : 0;
+    for (int i = tid; i < max(n_t, n_o); i += NT) {
+      unsigned long long rec = 0;
+      int oc = 0;
+      float ow[G];
+      if (i < n_t) rec = ld_dev(&ftie[tie_slot(i)]);
+      if (i < n_o) {
+        const int slot = S.tbase[sub] + i;
+        oc = ftc[slot];
+#pragma unroll
+        for (int g = 0; g < G; ++g) ow[g] = ftw[(size_t)slot * G + g];
+      }
+      if (i < n_t) tcache[i] = rec;
+      if (i < n_o) {
+        ownc[i] = oc;
+#pragma unroll
+        for (int g = 0; g < G; ++g) ownw[i * G + g] = ow[g];
+      }
+    }
+  }
+  // cluster and weights of the block's own tie i (a head-wide tie index)
+  auto own_add = [&](int i) {
+    const int t = i - own0;
+    int cl;
+    float w[G];
+    if (t < kOwnCap) {
+      cl = ownc[t];
+#pragma unroll
+      for (int g = 0; g < G; ++g) w[g] = ownw[t * G + g];
+    } else {
+      const int slot = S.tbase[sub] + t;
+      cl = ftc[slot];
+#pragma unroll
+      for (int g = 0; g < G; ++g) w[g] = ftw[(size_t)slot * G + g];
+    }
+    cl = min(max(cl, c0), c1 - 1);
+#pragma unroll
+    for (int g = 0; g < G; ++g) atomicAdd(&wsel[(cl - c0) * G + g], to_fixed(w[g]));
+  };
   // this block's rows of the head's exact list [sink | above | tie winners |
   // recent]: every row but the winners is known already
   const int n_rec = si.T - si.recent_beg;
@@ -751,14 +797,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       if (!is_winner(rec)) continue;
       const int row = si.ns + n_above + wi++;
       if (row >= lo && row < hi) frows[row] = (int32_t)(uint32_t)rec;
-      const int j = seg_of(S.tpre, P, i);
-      if (j == sub) {
-        const int slot = S.tbase[j] + (i - S.tpre[j]);
-        const int cl = min(max(ftc[slot], c0), c1 - 1);
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-          atomicAdd(&wsel[(cl - c0) * G + g], to_fixed(ftw[(size_t)slot * G + g]));
-      }
+      if (i >= own0 && i < S.tpre[sub + 1]) own_add(i);
     }
   } else if (r > 0) {
     int run = 0;
@@ -775,14 +814,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       if (win) {
         const int row = si.ns + n_above + run + ow;
         if (row >= lo && row < hi) frows[row] = (int32_t)(uint32_t)rec;
-        const int j = seg_of(S.tpre, P, i);
-        if (j == sub) {
-          const int slot = S.tbase[j] + (i - S.tpre[j]);
-          const int cl = min(max(ftc[slot], c0), c1 - 1);
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-            atomicAdd(&wsel[(cl - c0) * G + g], to_fixed(ftw[(size_t)slot * G + g]));
-        }
+        if (i >= own0 && i < S.tpre[sub + 1]) own_add(i);
       }
       run += tw;
     }
