@@ -143,7 +143,7 @@ WsLayout ws_layout(const Dims& d, bool dense) {
     l.wsel = o;       o = align_up(o + BH * d.L * d.G * sizeof(unsigned long long));
     l.rows = o;       o = align_up(o + BH * d.cap * sizeof(int32_t));
     l.n_rows = o;     o = align_up(o + BH * sizeof(int32_t));
-    l.fsync = o;      o = align_up(o + BH * 4 * sizeof(uint32_t));
+    l.fsync = o;      o = align_up(o + BH * 3 * kSyncStride * sizeof(uint32_t));
     l.fflags = o;     o = align_up(o + sizeof(uint32_t));
     l.fcnt = o;       o = align_up(o + BH * kMaxFusedP * sizeof(unsigned long long));
     l.fpart = o;      o = align_up(o + BH * d.G * kMaxFusedP * kPart * sizeof(float));

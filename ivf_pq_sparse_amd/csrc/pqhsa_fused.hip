@@ -126,7 +126,7 @@ __device__ void head_barrier(uint32_t* ctr, uint32_t n, uint32_t* flags) {
     // not the last to arrive: poll until the others have
     const unsigned long long t0 = wall_clock64();
     while (ld_dev(ctr) < n) {
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(8);
       if (wall_clock64() - t0 > kBarrierTimeout) {
         __hip_atomic_fetch_or(flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   using C = FusedCfg<G>;
   constexpr int NT = C::NT, NW = C::NW, NG = C::NG;
   constexpr int PT = 4;   // 64-entry tiles per scan round
-  constexpr int kIB = 2;  // attention items whose loads are in flight together
+  constexpr int kIB = G == 8 ? 2 : 4;  // attention items whose loads are in flight together
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ FusedStatic S;
   float* lut = reinterpret_cast<float*>(dyn);
@@ -311,7 +311,9 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   auto entry_at = [&](int c) { return min(max(off[c], 0), d.cap); };
   const int E0 = entry_at(c0), E1 = max(E0, entry_at(c1));
   const SeqInfo si = seq_info(d, a.ctx, a.ix.n_indexed, b);
-  uint32_t* sync = a.ws.fsync + (size_t)bh * 4;
+  // the head's three counters (barrier 1, barrier 2, finished blocks), each on
+  // its own cache line: heads and counters do not contend for one line
+  uint32_t* sync = a.ws.fsync + (size_t)bh * 3 * kSyncStride;
   uint32_t* ghist = a.ws.hist + (size_t)bh * kHistBins;
   uint32_t* keys = a.ws.keys + (size_t)bh * d.cap;
   float* qcg = a.ws.qc + (size_t)bh * d.L * G;
@@ -635,9 +637,14 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   if (tid == 0)
     st_dev(&a.ws.fcnt[(size_t)bh * kMaxFusedP + sub],
            ((unsigned long long)(uint32_t)nt << 32) | (uint32_t)na);
-  head_barrier(&sync[1], (uint32_t)P, a.ws.fflags);
+  head_barrier(&sync[kSyncStride], (uint32_t)P, a.ws.fflags);
 
   // ======================================================= phase 3: ties, rows, partials
+  // the queries for the exact rows (packed bf16, 8 dims per lane of a 16-lane
+  // row), loaded now so that their latency is hidden
+  uint4 qp[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) qp[g] = *reinterpret_cast<const uint4*>(qh + g * kD + (tid & 15) * 8);
   if (tid < 64) {
     unsigned long long v = 0;
     if (tid < P) v = ld_dev(&a.ws.fcnt[(size_t)bh * kMaxFusedP + tid]);
@@ -832,9 +839,6 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   }
   // exact rows and background clusters as one item list through 16-lane groups
   const int l16 = tid & 15, rg = tid >> 4;
-  uint4 qp[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) qp[g] = *reinterpret_cast<const uint4*>(qh + g * kD + l16 * 8);
   AttnState<G> st;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -946,7 +950,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   __syncthreads();
   if (tid == 0) {
     const uint32_t old =
-        __hip_atomic_fetch_add(&sync[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(&sync[2 * kSyncStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     S.last = old == (uint32_t)(P - 1);
   }
   __syncthreads();
@@ -1044,8 +1048,8 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   for (int i = tid; i < kHistBins; i += NT) st_dev(&ghist[i], 0u);
   if (tid == 0) {
     st_dev(&sync[0], 0u);
-    st_dev(&sync[1], 0u);
-    st_dev(&sync[2], 0u);
+    st_dev(&sync[kSyncStride], 0u);
+    st_dev(&sync[2 * kSyncStride], 0u);
   }
 }
 

@@ -34,6 +34,7 @@ constexpr int kBgWaves = 4;             // waves per background block
 constexpr int kBgBatch = 4;             // clusters whose loads a background wave issues together
 constexpr int kUploadChunk = 4096;      // tokens per counting-sort chunk
 constexpr int kMaxFusedP = 64;          // fused step: at most this many blocks per (b, h)
+constexpr int kSyncStride = 32;         // uint32s between fused-step counters (128 B)
 constexpr int kFusedWselMax = 1024;     // fused step: clusters per block x G held in LDS
 constexpr int kReuseSlab = 128;         // ring slots per search block
 constexpr int kReuseMinRows = 64;       // query reuse: fewest rows per split-K block
@@ -91,7 +92,8 @@ struct WsPtrs {
   int32_t* n_rows;     // [BH] exact rows (query reuse: partials to merge)
   float* partials;     // [B][Hq][n_parts][132]
   // fused step only
-  uint32_t* fsync;     // [BH][4] arrivals at the two per-head barriers, finished blocks
+  uint32_t* fsync;     // [BH][3][kSyncStride] arrivals at the two per-head barriers,
+                       //   finished blocks: each counter on a cache line of its own
   uint32_t* fflags;    // [1] bit 0: a barrier wait timed out
   unsigned long long* fcnt;  // [BH][kMaxFusedP] (above count | tie count << 32) per block
   float* fpart;        // [BH][G][kMaxFusedP][132] one partial per block and query head
