@@ -116,14 +116,22 @@ __device__ __forceinline__ float ld_dev(const float* p) {
 // (s_waitcnt vmcnt(0)); no cache write-back or invalidation.
 __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0xF70); }
 
-// All P blocks of a head arrive; returns when all have arrived or the time
-// bound has passed (then bit 0 of *flags is set).
-__device__ void head_barrier(uint32_t* ctr, uint32_t n, uint32_t* flags) {
+// A barrier of the P blocks of a head, in two halves so that a block can
+// issue loads of its own data while it waits.  Arrive: every thread's memory
+// operations have completed, then one thread adds to the head's counter (true
+// in thread 0 when this block arrived last).  Wait: thread 0 polls until all
+// have arrived or the time bound has passed (then bit 0 of *flags is set).
+__device__ bool barrier_arrive(uint32_t* ctr, uint32_t n) {
   wait_mem();
   __syncthreads();
-  if (threadIdx.x == 0 &&
-      __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 < n) {
-    // not the last to arrive: poll until the others have
+  bool last = false;
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 >= n;
+  return last;
+}
+
+__device__ void barrier_wait(uint32_t* ctr, uint32_t n, uint32_t* flags, bool last) {
+  if (threadIdx.x == 0 && !last) {
     const unsigned long long t0 = wall_clock64();
     while (ld_dev(ctr) < n) {
       __builtin_amdgcn_s_sleep(8);
@@ -549,7 +557,16 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       if (v) __hip_atomic_fetch_add(&ghist[i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  head_barrier(&sync[0], (uint32_t)P, a.ws.fflags);
+  const bool last1 = barrier_arrive(&sync[0], (uint32_t)P);
+  // while waiting: this block's first keys for the classification below
+  constexpr int kPer = 16;
+  uint32_t pk[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int e = E0 + u * NT + tid;
+    pk[u] = e < E1 ? keys[e] : 0u;
+  }
+  barrier_wait(&sync[0], (uint32_t)P, a.ws.fflags, last1);
 
   // ======================================================= phase 2: threshold bucket
   // the head's histogram from read_lo up: exact there, because every block
@@ -578,7 +595,6 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   // tid): count, one block scan, list the chosen entries in LDS (above ones
   // first, each group in thread order), then record them one list entry per
   // thread.  Entries beyond the list's capacity are recorded by their thread.
-  constexpr int kPer = 16;
   constexpr int kChunk = NT * kPer;
   constexpr int kListCap = (int)(C::kHBytes / sizeof(int));
   int* elist = reinterpret_cast<int*>(hist);
@@ -607,7 +623,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
         const int e = cb + u * NT + tid;
-        const uint32_t kv = e < E1 ? keys[e] : 0u;
+        const uint32_t kv = cb == E0 ? pk[u] : (e < E1 ? keys[e] : 0u);
         const int bucket = (int)(kv >> (32 - kHistBits));
         ca += kv != 0u && bucket > beta;
         ct += kv != 0u && bucket == beta;
@@ -637,7 +653,23 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   if (tid == 0)
     st_dev(&a.ws.fcnt[(size_t)bh * kMaxFusedP + sub],
            ((unsigned long long)(uint32_t)nt << 32) | (uint32_t)na);
-  head_barrier(&sync[kSyncStride], (uint32_t)P, a.ws.fflags);
+  const bool last2 = barrier_arrive(&sync[kSyncStride], (uint32_t)P);
+  // while waiting: this block's own tie records' clusters and weights into LDS
+  // (the histogram region is free until the background logits), so that
+  // placing its winners needs no global load
+  constexpr int kOwnCap = (int)(C::kHBytes / ((1 + G) * sizeof(float)));
+  float* ownw = reinterpret_cast<float*>(hist);                  // [kOwnCap][G]
+  int* ownc = reinterpret_cast<int*>(ownw + (size_t)kOwnCap * G);   // [kOwnCap]
+  for (int i = tid; i < min(nt, kOwnCap); i += NT) {
+    const int oc = ftc[E0 + i];
+    float ow[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) ow[g] = ftw[(size_t)(E0 + i) * G + g];
+    ownc[i] = oc;
+#pragma unroll
+    for (int g = 0; g < G; ++g) ownw[i * G + g] = ow[g];
+  }
+  barrier_wait(&sync[kSyncStride], (uint32_t)P, a.ws.fflags, last2);
 
   // ======================================================= phase 3: ties, rows, partials
   // the queries for the exact rows (packed bf16, 8 dims per lane of a 16-lane
@@ -670,35 +702,9 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   auto tie_rec = [&](int i) -> unsigned long long {
     return cached ? tcache[i] : ld_dev(&ftie[tie_slot(i)]);
   };
-  // The tie records into LDS, and with them this block's own tie records'
-  // clusters and weights (the histogram region is free until the background
-  // logits), so that placing the winners needs no global load.
-  constexpr int kOwnCap = (int)(C::kHBytes / ((1 + G) * sizeof(float)));
-  float* ownw = reinterpret_cast<float*>(hist);                  // [kOwnCap][G]
-  int* ownc = reinterpret_cast<int*>(ownw + (size_t)kOwnCap * G);   // [kOwnCap]
   const int own0 = S.tpre[sub];
-  {
-    const int n_t = (r > 0 && cached) ? n_tie : 0;
-    const int n_o = r > 0 ? min(S.tpre[sub + 1] - own0, kOwnCap) : 0;
-    for (int i = tid; i < max(n_t, n_o); i += NT) {
-      unsigned long long rec = 0;
-      int oc = 0;
-      float ow[G];
-      if (i < n_t) rec = ld_dev(&ftie[tie_slot(i)]);
-      if (i < n_o) {
-        const int slot = S.tbase[sub] + i;
-        oc = ftc[slot];
-#pragma unroll
-        for (int g = 0; g < G; ++g) ow[g] = ftw[(size_t)slot * G + g];
-      }
-      if (i < n_t) tcache[i] = rec;
-      if (i < n_o) {
-        ownc[i] = oc;
-#pragma unroll
-        for (int g = 0; g < G; ++g) ownw[i * G + g] = ow[g];
-      }
-    }
-  }
+  if (r > 0 && cached)
+    for (int i = tid; i < n_tie; i += NT) tcache[i] = ld_dev(&ftie[tie_slot(i)]);
   // cluster and weights of the block's own tie i (a head-wide tie index)
   auto own_add = [&](int i) {
     const int t = i - own0;
