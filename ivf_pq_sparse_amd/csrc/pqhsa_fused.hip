@@ -859,49 +859,65 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   const uint16_t* kc = a.kc + l16 * 8;
   const uint16_t* vc = a.vc + l16 * 8;
   const float* means = a.ix.means + (size_t)bh * d.L * kD + l16 * 8;
-  for (int ph = 0; ph < n_items; ph += C::kItems) {
-    const int n = min(C::kItems, n_items - ph);
+  // Items are staged up to kStage at a time (their cache offsets in LDS); a
+  // 16-lane group takes items rg, rg + NG, ... in that order, with the loads
+  // of the next kIB of them in flight while it computes.
+  constexpr int kStage = (int)((C::kHBytes - 4096) / sizeof(long long));
+  for (int ph = 0; ph < n_items; ph += kStage) {
+    const int n = min(kStage, n_items - ph);
     __syncthreads();
-    if (tid < n) {
-      const int it = ph + tid;
-      if (it < nr) {
-        const int p = min(max(frows[lo + it], 0), d.cap - 1);
-        int page = tab[p >> 4];
-        page = min(max(page, 0), d.num_pages - 1);
-        ioff[tid] = ((long long)(page * kPage + (p & (kPage - 1))) * d.Hkv + h) * kD;
-      } else {
-        ioff[tid] = -1 - (long long)(it - nr);
+    {
+      // a thread's rows, then their pages, each round of loads issued at once
+      constexpr int kPerT = (kStage + NT - 1) / NT;
+      int pr[kPerT], pg[kPerT];
+#pragma unroll
+      for (int i = 0; i < kPerT; ++i) {
+        const int t = tid + i * NT, it = ph + t;
+        pr[i] = (t < n && it < nr) ? min(max(frows[lo + it], 0), d.cap - 1) : -1;
       }
-    }
-    __syncthreads();
-    // the group's items two at a time: both loads out, then both computed
 #pragma unroll
-    for (int u0 = 0; u0 < C::kItemsPerGroup; u0 += kIB) {
-      uint4 kw[kIB], vw[kIB];
+      for (int i = 0; i < kPerT; ++i) pg[i] = pr[i] >= 0 ? tab[pr[i] >> 4] : 0;
 #pragma unroll
-      for (int u = 0; u < kIB; ++u) {
-        const int j = rg + (u0 + u) * NG;
-        kw[u] = vw[u] = make_uint4(0, 0, 0, 0);
-        if (j < n) {
-          const long long o = ioff[j];
-          if (o >= 0) {
-            kw[u] = *reinterpret_cast<const uint4*>(kc + o);
-            vw[u] = *reinterpret_cast<const uint4*>(vc + o);
+      for (int i = 0; i < kPerT; ++i) {
+        const int t = tid + i * NT, it = ph + t;
+        if (t < n) {
+          if (it < nr) {
+            const int page = min(max(pg[i], 0), d.num_pages - 1);
+            ioff[t] = ((long long)(page * kPage + (pr[i] & (kPage - 1))) * d.Hkv + h) * kD;
           } else {
-            const float* mu = means + (size_t)(c0 + (int)(-1 - o)) * kD;
-            kw[u] = *reinterpret_cast<const uint4*>(mu);
-            vw[u] = *reinterpret_cast<const uint4*>(mu + 4);
+            ioff[t] = -1 - (long long)(it - nr);
           }
         }
       }
+    }
+    __syncthreads();
+    auto load_item = [&](int j, uint4& kw, uint4& vw) {
+      kw = vw = make_uint4(0, 0, 0, 0);
+      if (j < n) {
+        const long long o = ioff[j];
+        if (o >= 0) {
+          kw = *reinterpret_cast<const uint4*>(kc + o);
+          vw = *reinterpret_cast<const uint4*>(vc + o);
+        } else {
+          const float* mu = means + (size_t)(c0 + (int)(-1 - o)) * kD;
+          kw = *reinterpret_cast<const uint4*>(mu);
+          vw = *reinterpret_cast<const uint4*>(mu + 4);
+        }
+      }
+    };
+    uint4 kw[kIB], vw[kIB];
+#pragma unroll
+    for (int u = 0; u < kIB; ++u) load_item(rg + u * NG, kw[u], vw[u]);
+    for (int j0 = rg; j0 < n; j0 += kIB * NG) {
 #pragma unroll
       for (int u = 0; u < kIB; ++u) {
-        const int j = rg + (u0 + u) * NG;
+        const int j = j0 + u * NG;
         if (j < n) {
           const long long o = ioff[j];
           if (o >= 0) attend_row_pk<G>(st, qp, d.scale_log2, kw[u], vw[u]);
           else attend_bg<G>(st, sbg + (int)(-1 - o) * G, kw[u], vw[u]);
         }
+        load_item(j + kIB * NG, kw[u], vw[u]);
       }
     }
   }
