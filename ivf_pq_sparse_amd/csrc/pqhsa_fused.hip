@@ -75,6 +75,7 @@ struct FusedCfg {
 };
 
 struct FusedStatic {
+  int nextc;        // the scan's next unclaimed cluster of the block
   int sh[40];
   uint32_t rh[256];
   int res[4];
@@ -451,6 +452,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     __syncthreads();   // the staged q is read for the last time above
     for (int i = tid; i < kHistBins; i += NT) hist[i] = 0u;
     for (int i = tid; i < ncl * G; i += NT) wsel[i] = 0ull;
+    if (tid == 0) S.nextc = c0 + NW;
   }
   __syncthreads();
   float qc[G];
@@ -463,11 +465,21 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   int base = e0;
   // one round of PT tiles; the next round (more of this cluster, or the first
   // of the wave's next one) is issued before this one is computed
+  const bool claims = ncl > 4 * NW;
   auto round = [&](FRound<G, PT>& now, FRound<G, PT>& nxt) {
     int nc = c, nbase = base + 64 * PT, ne0 = e0, ne1 = e1;
     const bool last = nbase >= e1;
     if (last) {
-      nc = c + NW;
+      // the wave's next cluster: with many clusters per wave the block's next
+      // unclaimed one, so that the waves finish together whatever the cluster
+      // sizes; with few, the next in a fixed stride (no claim on the path)
+      if (claims) {
+        int claim = 0;
+        if (lane == 0) claim = atomicAdd(&S.nextc, 1);
+        nc = __builtin_amdgcn_readfirstlane(claim);
+      } else {
+        nc = c + NW;
+      }
       if (nc < c1) {
         ne0 = entry_at(nc);
         ne1 = max(ne0, entry_at(nc + 1));
