@@ -277,3 +277,42 @@ def test_repeated_steps_are_deterministic():
         else:
             assert torch.equal(sel, first[1])
             assert torch.equal(out, first[0])
+
+
+def test_tie_bucket_larger_than_the_lds_caches():
+    # 90 % of the candidates copy the top candidate's list and codes: the
+    # threshold bucket holds ~118K exact ties, more than the fused step's LDS
+    # tie cache and, per block, more than its LDS staging of its own ties; the
+    # winners are the lowest positions of the tie
+    T = 131072
+    inp = make_step_inputs(0, context_lens=[T], num_lists=64, budget_bp=100, noise=0.0,
+                           workload_id=16)
+    ref0 = oracle_with_details(inp)
+    kap, cand = ref0["kappa"][(0, 0)], ref0["candidates"][(0, 0)]
+    src = int(cand[np.argmax(kap[cand])])          # the largest key: the tie is the bucket
+    rng = np.random.default_rng(16)
+    dups = np.sort(rng.choice(cand[cand != src], size=int(0.9 * cand.size), replace=False))
+    inp.list_ids[0, 0, dups] = inp.list_ids[0, 0, src]
+    inp.codes[0, 0, dups] = inp.codes[0, 0, src]
+    log("[pqhsa] 118K exact ties at 128K")
+    g, ref, _ = parity(inp, what="huge tie bucket")
+    sel = g["selected"][(0, 0)]
+    tied = np.sort(np.concatenate([dups, [src]]))
+    above = np.setdiff1d(sel, tied)
+    k = ref["k"][(0, 0)]
+    assert tied.size > 8192 and above.size == 0
+    # the tied key is the largest: the selection is the tie's lowest positions
+    assert np.array_equal(sel, tied[:k])
+
+
+def test_full_budget_long_context_few_clusters():
+    # 8 clusters over 64K tokens: 8 blocks of 8192 entries each, so the
+    # selected-entry list and the attention item staging of a block both
+    # overflow their LDS capacity and take their second paths
+    import oracle
+    inp = make_step_inputs(0, context_lens=[65536], num_lists=8, budget_bp=10000,
+                           workload_id=17)
+    log("[pqhsa] budget 100 % at 64K over 8 clusters")
+    g = run_gpu(inp)
+    check_output(g["O"], oracle.dense_step(inp), "budget 100% at 64K vs dense")
+    parity(inp, what="budget 100 % at 64K, 8 clusters")
