@@ -10,12 +10,14 @@
 //   list = argmin_c ||K_t - C_c||^2, code_m = argmin_j ||r^(m) - B_m[j]||^2,
 //   r = K_t - C[list], lowest index on equal distances, fp32 arithmetic.
 //
-//   k_append_encode  one block per (b, h, 16 new tokens): keys from the paged
-//                    cache into LDS; every thread scans its share of the
-//                    centroids for all 16 keys, a block reduction picks each
-//                    key's list; then thread (key, subspace) scans the 256
-//                    codewords of its subspace from an LDS copy of the
-//                    codebook.  Writes the token-order list ids and codes.
+//   k_append_assign  one block per (b, h, 64 new tokens): keys from the paged
+//                    cache and 64-centroid chunks (the next chunk's loads in
+//                    flight) in padded LDS rows; each thread owns a 4 token x
+//                    4 centroid tile of distances, a 16-lane reduction picks
+//                    each key's list.  Writes the token-order list ids.
+//   k_append_pq      one block per (b, h, 64 new tokens) with the codebook in
+//                    LDS: thread (4 tokens, subspace) forms the residual slices
+//                    and scans the subspace's 256 codewords.  Writes the codes.
 //   regroup          new cluster offsets from the new tokens' counts; old
 //                    entries move (from a snapshot) by the number of new
 //                    entries in clusters before theirs; new tokens are placed
@@ -29,18 +31,15 @@ namespace pqhsa {
 
 namespace {
 
-constexpr int kEncTokens = 16;     // new tokens per encode block
-constexpr int kEncThreads = 256;   // = kEncTokens * kM
+constexpr int kEncTokens = 64;     // new tokens per assignment / code block
+constexpr int kEncThreads = 256;
+constexpr int kAsgCents = 64;      // centroids per LDS chunk of the assignment
+// LDS rows of keys and centroids, padded so that 16 consecutive rows read by
+// one 16-lane group start 4 banks apart
+constexpr int kRowPad = kD + 4;
 // codebook rows padded by 4 floats per subspace so that the 16 subspaces read
 // by one wave fall on different LDS banks
 constexpr int kCbStride = kKsub * kDsub + 4;
-
-struct EncodeLds {
-  float key[kEncTokens][kD];          // keys, then residuals
-  float best_d[4][kEncTokens];        // per-wave best distance and centroid
-  int best_c[4][kEncTokens];
-  int list[kEncTokens];
-};
 
 __device__ __forceinline__ void better(float& d, int& c, float d2, int c2) {
   if (d2 < d || (d2 == d && c2 < c)) { d = d2; c = c2; }
@@ -48,19 +47,20 @@ __device__ __forceinline__ void better(float& d, int& c, float d2, int c2) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kEncThreads) void k_append_encode(AppendArgs a) {
-  extern __shared__ float cb[];        // [16][kCbStride]
-  __shared__ EncodeLds sh;
+__global__ __launch_bounds__(kEncThreads) void k_append_assign(AppendArgs a) {
+  extern __shared__ __align__(16) float alds[];
+  float* keyl = alds;                          // [64][kRowPad]
+  float* cenl = alds + kEncTokens * kRowPad;   // [64][kRowPad]
   const Dims& d = a.d;
   const int bh = blockIdx.x;
   const int b = bh / d.Hkv, h = bh % d.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int old_n = min(max(a.ix.n_indexed[b], 0), d.cap);
   const int new_n = min(max(a.new_n_indexed[b], 0), d.cap);
   const int t0 = old_n + blockIdx.y * kEncTokens;
   const int nt = min(kEncTokens, new_n - t0);
   if (nt <= 0) return;
-  // keys of the block's tokens (bf16 -> fp32), 8 dims per thread
+  // keys of the block's tokens (bf16 -> fp32), 8 dims per thread and pass
   const int32_t* tab = a.table + (size_t)b * d.max_pages;
   for (int i = tid; i < kEncTokens * (kD / 8); i += kEncThreads) {
     const int tk = i / (kD / 8), part = i % (kD / 8);
@@ -74,93 +74,161 @@ __global__ __launch_bounds__(kEncThreads) void k_append_encode(AppendArgs a) {
       f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
       f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) sh.key[tk][part * 8 + u] = f[u];
+    float4* dst = reinterpret_cast<float4*>(keyl + tk * kRowPad + part * 8);
+    dst[0] = make_float4(f[0], f[1], f[2], f[3]);
+    dst[1] = make_float4(f[4], f[5], f[6], f[7]);
   }
-  // the codebook of this (b, h) into LDS (used after the assignment)
+  // thread tile: tokens tq*4 + i, centroids c0 + cq + 16 j of each chunk
+  const int tq = tid / 16, cq = tid % 16;
+  float bd[4];
+  int bc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { bd[i] = INFINITY; bc[i] = 0x7fffffff; }
+  const float4* cen4 = reinterpret_cast<const float4*>(a.ix.centroids + (size_t)bh * d.L * kD);
+  constexpr int kPer = kAsgCents * (kD / 4) / kEncThreads;   // float4 of a chunk per thread
+  float4 pre[kPer];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int idx = tid + u * kEncThreads, row = idx / (kD / 4), q = idx % (kD / 4);
+      pre[u] = c0 + row < d.L ? cen4[(size_t)(c0 + row) * (kD / 4) + q]
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  load_chunk(0);
+  const float4* keyl4 = reinterpret_cast<const float4*>(keyl);
+  const float4* cenl4 = reinterpret_cast<const float4*>(cenl);
+  for (int c0 = 0; c0 < d.L; c0 += kAsgCents) {
+    __syncthreads();   // the previous chunk is no longer read
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int idx = tid + u * kEncThreads, row = idx / (kD / 4), q = idx % (kD / 4);
+      reinterpret_cast<float4*>(cenl + row * kRowPad)[q] = pre[u];
+    }
+    __syncthreads();
+    if (c0 + kAsgCents < d.L) load_chunk(c0 + kAsgCents);
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+#pragma unroll 2
+    for (int q4 = 0; q4 < kD / 4; ++q4) {
+      float4 kv[4], cv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kv[i] = keyl4[(tq * 4 + i) * (kRowPad / 4) + q4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cv[j] = cenl4[(cq + 16 * j) * (kRowPad / 4) + q4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float e0 = kv[i].x - cv[j].x, e1 = kv[i].y - cv[j].y, e2 = kv[i].z - cv[j].z,
+                      e3 = kv[i].w - cv[j].w;
+          float x = acc[i][j];
+          x = fmaf(e0, e0, x);
+          x = fmaf(e1, e1, x);
+          x = fmaf(e2, e2, x);
+          x = fmaf(e3, e3, x);
+          acc[i][j] = x;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = c0 + cq + 16 * j;
+        if (c < d.L) better(bd[i], bc[i], acc[i][j], c);
+      }
+  }
+  // each token's best over the 16 lanes of its row
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+      const float d2 = __shfl_xor(bd[i], o);
+      const int c2 = __shfl_xor(bc[i], o);
+      better(bd[i], bc[i], d2, c2);
+    }
+  }
+  if (cq == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tk = tq * 4 + i;
+      if (tk < nt) a.list_ids[(size_t)bh * d.cap + t0 + tk] = min(max(bc[i], 0), d.L - 1);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kEncThreads) void k_append_pq(AppendArgs a) {
+  extern __shared__ __align__(16) float cb[];   // [16][kCbStride]
+  const Dims& d = a.d;
+  const int bh = blockIdx.x;
+  const int b = bh / d.Hkv, h = bh % d.Hkv;
+  const int tid = threadIdx.x;
+  const int old_n = min(max(a.ix.n_indexed[b], 0), d.cap);
+  const int new_n = min(max(a.new_n_indexed[b], 0), d.cap);
+  const int t0 = old_n + blockIdx.y * kEncTokens;
+  const int nt = min(kEncTokens, new_n - t0);
+  if (nt <= 0) return;
+  // the codebook of this (b, h) into LDS
   const float* cbg = a.ix.codebooks + (size_t)bh * kM * kKsub * kDsub;
   for (int i = tid; i < kM * kKsub * kDsub / 4; i += kEncThreads) {
     const int m = i / (kKsub * kDsub / 4), r = i % (kKsub * kDsub / 4);
     *reinterpret_cast<float4*>(cb + m * kCbStride + r * 4) =
         reinterpret_cast<const float4*>(cbg)[i];
   }
-  __syncthreads();
-  // assignment: thread scans centroids tid, tid + 256, ... in ascending order
-  float bd[kEncTokens];
-  int bc[kEncTokens];
-#pragma unroll
-  for (int k = 0; k < kEncTokens; ++k) { bd[k] = INFINITY; bc[k] = 0x7fffffff; }
+  // residual slices r^(m) = K_t - C[list_t] of this thread's tokens tq*4 + i
+  const int m = tid % kM, tq = tid / kM;
+  const int32_t* tab = a.table + (size_t)b * d.max_pages;
   const float* cen = a.ix.centroids + (size_t)bh * d.L * kD;
-  for (int c = tid; c < d.L; c += kEncThreads) {
-    float acc[kEncTokens];
+  float r[4][8];
 #pragma unroll
-    for (int k = 0; k < kEncTokens; ++k) acc[k] = 0.0f;
-    const float4* cp = reinterpret_cast<const float4*>(cen + (size_t)c * kD);
-    for (int q4 = 0; q4 < kD / 4; ++q4) {
-      const float4 cv = cp[q4];
+  for (int i = 0; i < 4; ++i) {
+    const int tk = tq * 4 + i;
 #pragma unroll
-      for (int k = 0; k < kEncTokens; ++k) {
-        const float4 kv = *reinterpret_cast<const float4*>(&sh.key[k][q4 * 4]);
-        const float d0 = kv.x - cv.x, d1 = kv.y - cv.y, d2 = kv.z - cv.z, d3 = kv.w - cv.w;
-        acc[k] = fmaf(d0, d0, acc[k]);
-        acc[k] = fmaf(d1, d1, acc[k]);
-        acc[k] = fmaf(d2, d2, acc[k]);
-        acc[k] = fmaf(d3, d3, acc[k]);
-      }
+    for (int u = 0; u < 8; ++u) r[i][u] = 0.0f;
+    if (tk < nt) {
+      const int t = t0 + tk;
+      const int list = min(max(a.list_ids[(size_t)bh * d.cap + t], 0), d.L - 1);
+      int page = tab[t >> 4];
+      page = min(max(page, 0), d.num_pages - 1);
+      const uint4 w = *reinterpret_cast<const uint4*>(
+          a.kc + ((size_t)(page * kPage + (t & (kPage - 1))) * d.Hkv + h) * kD + m * kDsub);
+      const float4 c0v = *reinterpret_cast<const float4*>(cen + (size_t)list * kD + m * kDsub);
+      const float4 c1v = *reinterpret_cast<const float4*>(cen + (size_t)list * kD + m * kDsub + 4);
+      r[i][0] = bf16_lo(w.x) - c0v.x; r[i][1] = bf16_hi(w.x) - c0v.y;
+      r[i][2] = bf16_lo(w.y) - c0v.z; r[i][3] = bf16_hi(w.y) - c0v.w;
+      r[i][4] = bf16_lo(w.z) - c1v.x; r[i][5] = bf16_hi(w.z) - c1v.y;
+      r[i][6] = bf16_lo(w.w) - c1v.z; r[i][7] = bf16_hi(w.w) - c1v.w;
     }
+  }
+  __syncthreads();
+  float best[4];
+  int code[4];
 #pragma unroll
-    for (int k = 0; k < kEncTokens; ++k) better(bd[k], bc[k], acc[k], c);
-  }
-  // block argmin per token: wave butterfly, then the 4 waves
-#pragma unroll
-  for (int k = 0; k < kEncTokens; ++k) {
-    float dv = bd[k];
-    int cv = bc[k];
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float d2 = __shfl_xor(dv, o);
-      const int c2 = __shfl_xor(cv, o);
-      better(dv, cv, d2, c2);
-    }
-    if (lane == 0) { sh.best_d[wave][k] = dv; sh.best_c[wave][k] = cv; }
-  }
-  __syncthreads();
-  if (tid < kEncTokens) {
-    float dv = sh.best_d[0][tid];
-    int cv = sh.best_c[0][tid];
-    for (int w = 1; w < 4; ++w) better(dv, cv, sh.best_d[w][tid], sh.best_c[w][tid]);
-    sh.list[tid] = min(max(cv, 0), d.L - 1);
-  }
-  __syncthreads();
-  // residuals in place
-  for (int i = tid; i < kEncTokens * kD; i += kEncThreads) {
-    const int tk = i / kD, dim = i % kD;
-    sh.key[tk][dim] -= cen[(size_t)sh.list[tk] * kD + dim];
-  }
-  __syncthreads();
-  // PQ codes: thread (token, subspace) scans the 256 codewords in order
-  const int tk = tid / kM, m = tid % kM;
-  const float4 r0 = *reinterpret_cast<const float4*>(&sh.key[tk][m * kDsub]);
-  const float4 r1 = *reinterpret_cast<const float4*>(&sh.key[tk][m * kDsub + 4]);
-  float best = INFINITY;
-  int code = 0;
+  for (int i = 0; i < 4; ++i) { best[i] = INFINITY; code[i] = 0; }
   const float* cbm = cb + m * kCbStride;
+#pragma unroll 4
   for (int j = 0; j < kKsub; ++j) {
     const float4 w0 = *reinterpret_cast<const float4*>(cbm + j * kDsub);
     const float4 w1 = *reinterpret_cast<const float4*>(cbm + j * kDsub + 4);
-    float e = r0.x - w0.x, acc = e * e;
-    e = r0.y - w0.y; acc = fmaf(e, e, acc);
-    e = r0.z - w0.z; acc = fmaf(e, e, acc);
-    e = r0.w - w0.w; acc = fmaf(e, e, acc);
-    e = r1.x - w1.x; acc = fmaf(e, e, acc);
-    e = r1.y - w1.y; acc = fmaf(e, e, acc);
-    e = r1.z - w1.z; acc = fmaf(e, e, acc);
-    e = r1.w - w1.w; acc = fmaf(e, e, acc);
-    if (acc < best) { best = acc; code = j; }
+    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float e = r[i][0] - wv[0], acc = e * e;
+#pragma unroll
+      for (int u = 1; u < 8; ++u) {
+        e = r[i][u] - wv[u];
+        acc = fmaf(e, e, acc);
+      }
+      if (acc < best[i]) { best[i] = acc; code[i] = j; }
+    }
   }
-  if (tk < nt) {
-    const int t = t0 + tk;
-    a.codes[((size_t)bh * d.cap + t) * kM + m] = (uint8_t)code;
-    if (m == 0) a.list_ids[(size_t)bh * d.cap + t] = sh.list[tk];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tk = tq * 4 + i;
+    if (tk < nt) a.codes[((size_t)bh * d.cap + t0 + tk) * kM + m] = (uint8_t)code[i];
   }
 }
 
@@ -275,46 +343,99 @@ __global__ __launch_bounds__(256) void k_append_move(AppendArgs a) {
 // One wave per (b, h): the new tokens in token order, each after the old
 // entries of its cluster and the earlier new ones (rank inside a 64-token
 // tile by comparing list ids, running counts per cluster in LDS).
-__global__ __launch_bounds__(64) void k_append_place(AppendArgs a) {
-  extern __shared__ int32_t run[];     // [L] new tokens placed so far per cluster
-  __shared__ int32_t tile[64];
+// Place the new tokens of one (b, h) after their clusters' old entries, in
+// token order, kPlaceTile tokens at a time.  The tile's list ids go to LDS;
+// W waves each take a contiguous chunk of it and count its tokens per cluster;
+// a prefix over the chunks gives every chunk its first slot in each cluster
+// (the cluster's next free slot plus the earlier chunks' tokens); then each
+// wave gives its tokens their slots, 64 at a time, the earlier tokens of the
+// same cluster among the 64 read lane by lane from registers; finally all
+// threads copy the entries to their slots.
+constexpr int kPlaceTile = 4096;
+
+// chunks of a tile: as many as up to 16 waves, within 128 KB of counters
+__host__ __device__ inline int place_chunks(int L) { return min(16, max(1, 32768 / L - 1)); }
+
+__global__ __launch_bounds__(1024) void k_append_place(AppendArgs a) {
+  extern __shared__ int32_t slot[];    // [W][L] chunk counts, then chunk slots; [L] next free
+  __shared__ int32_t lid[kPlaceTile];  // a tile's clusters, then their slots (-1: none)
   const Dims& d = a.d;
+  const int L = d.L;
+  const int W = place_chunks(L);
+  int32_t* nextf = slot + (size_t)W * L;
   const int bh = blockIdx.x;
   const int b = bh / d.Hkv;
-  const int lane = threadIdx.x;
-  for (int c = lane; c < d.L; c += 64) run[c] = 0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int old_n = min(max(a.ix.n_indexed[b], 0), d.cap);
   const int new_n = min(max(a.new_n_indexed[b], 0), d.cap);
   const size_t base = (size_t)bh * d.cap;
-  const int32_t* off = a.ix.list_off + (size_t)bh * (d.L + 1);
-  const int32_t* oo = a.old_off + (size_t)bh * (d.L + 1);
-  __syncthreads();
-  for (int s = old_n; s < new_n; s += 64) {
-    const int t = s + lane;
-    int c = -1;
-    if (t < new_n) {
-      c = a.list_ids[base + t];
-      if (c < 0 || c >= d.L) c = -1;
+  const int32_t* off = a.ix.list_off + (size_t)bh * (L + 1);
+  const int32_t* oo = a.old_off + (size_t)bh * (L + 1);
+  // a cluster's new entries start after its old ones, at its new offset
+  for (int c = tid; c < L; c += blockDim.x) nextf[c] = off[c] + (oo[c + 1] - oo[c]);
+  for (int s0 = old_n; s0 < new_n; s0 += kPlaceTile) {
+    const int n = min(kPlaceTile, new_n - s0);
+    const int chunk = (n + W - 1) / W;
+    for (int i = tid; i < n; i += blockDim.x) {
+      const int c = a.list_ids[base + s0 + i];
+      lid[i] = (c < 0 || c >= L) ? -1 : c;
     }
-    tile[lane] = c;
+    for (int i = tid; i < W * L; i += blockDim.x) slot[i] = 0;
     __syncthreads();
-    int rank = 0, same = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int cj = tile[j];
-      same += (cj == c);
-      rank += (cj == c) & (j < lane);
-    }
-    if (c >= 0) {
-      const int dst = off[c] + (oo[c + 1] - oo[c]) + run[c] + rank;
-      if (dst >= 0 && dst < d.cap) {
-        reinterpret_cast<uint4*>(a.ix.codes)[base + dst] =
-            reinterpret_cast<const uint4*>(a.codes)[base + t];
-        a.ix.pos[base + dst] = t;
-        a.ix.ent_list[base + dst] = c;
+    if (wave < W) {
+      const int e = min(n, (wave + 1) * chunk);
+      for (int i = wave * chunk + lane; i < e; i += 64) {
+        const int c = lid[i];
+        if (c >= 0) atomicAdd(&slot[wave * L + c], 1);
       }
     }
     __syncthreads();
-    if (c >= 0 && rank == same - 1) run[c] += same;
+    for (int c = tid; c < L; c += blockDim.x) {
+      int run = nextf[c];
+      for (int w = 0; w < W; ++w) {
+        const int t = slot[w * L + c];
+        slot[w * L + c] = run;
+        run += t;
+      }
+      nextf[c] = run;
+    }
+    __syncthreads();
+    if (wave < W) {
+      int32_t* sw = slot + wave * L;
+      const int e = min(n, (wave + 1) * chunk);
+      for (int g = wave * chunk; g < e; g += 64) {
+        const int i = g + lane;
+        const int c = i < e ? lid[i] : -1;
+        int rank = 0, same = 0;
+#pragma unroll
+        for (int j = 0; j < 64; ++j) {
+          const int cj = __builtin_amdgcn_readlane(c, j);
+          same += (cj == c);
+          rank += (cj == c) & (j < lane);
+        }
+        int dst = -1;
+        if (c >= 0) {
+          dst = sw[c] + rank;
+          if (dst < 0 || dst >= d.cap) dst = -1;
+        }
+        // every lane has read its cluster's slot before any lane moves it
+        __builtin_amdgcn_wave_barrier();
+        if (i < e) lid[i] = dst;
+        if (c >= 0 && rank == same - 1) sw[c] += same;
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += blockDim.x) {
+      const int dst = lid[i];
+      if (dst >= 0) {
+        const int t = s0 + i;
+        reinterpret_cast<uint4*>(a.ix.codes)[base + dst] =
+            reinterpret_cast<const uint4*>(a.codes)[base + t];
+        a.ix.pos[base + dst] = t;
+        a.ix.ent_list[base + dst] = a.list_ids[base + t];
+      }
+    }
     __syncthreads();
   }
 }
@@ -324,7 +445,11 @@ hipError_t launch_append_regroup(const AppendArgs& a, hipStream_t st) {
   const int BH = d.B * d.Hkv;
   hipLaunchKernelGGL(k_append_offsets, dim3(BH), dim3(1024), d.L * sizeof(int32_t), st, a);
   hipLaunchKernelGGL(k_append_move, dim3((d.cap + 255) / 256, BH), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_append_place, dim3(BH), dim3(64), d.L * sizeof(int32_t), st, a);
+  const size_t plds = (size_t)(place_chunks(d.L) + 1) * d.L * sizeof(int32_t);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_append_place),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_append_place, dim3(BH), dim3(1024), plds, st, a);
   return hipGetLastError();
 }
 
@@ -332,11 +457,16 @@ hipError_t launch_append_encode(const AppendArgs& a, int max_new, hipStream_t st
   const int BH = a.d.B * a.d.Hkv;
   const int tiles = (max_new + kEncTokens - 1) / kEncTokens;
   if (tiles == 0) return hipSuccess;
-  const size_t lds = (size_t)kM * kCbStride * sizeof(float);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_append_encode),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const size_t alds = (size_t)2 * kEncTokens * kRowPad * sizeof(float);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_append_assign),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)alds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_append_encode, dim3(BH, tiles), dim3(kEncThreads), lds, st, a);
+  hipLaunchKernelGGL(k_append_assign, dim3(BH, tiles), dim3(kEncThreads), alds, st, a);
+  const size_t plds = (size_t)kM * kCbStride * sizeof(float);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_append_pq),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_append_pq, dim3(BH, tiles), dim3(kEncThreads), plds, st, a);
   return hipGetLastError();
 }
 

@@ -36,7 +36,13 @@ def sq_dist(x: np.ndarray, c: np.ndarray) -> np.ndarray:
     """Squared Euclidean distances, x [n, d] against c [k, d] -> [n, k], float64."""
     x = np.asarray(x, np.float64)
     c = np.asarray(c, np.float64)
-    return ((x[:, None, :] - c[None, :, :]) ** 2).sum(axis=-1)
+    # rows in batches, only to bound the [rows, k, d] temporary; every entry
+    # is the same sum of squared differences
+    out = np.empty((x.shape[0], c.shape[0]))
+    rows = max(1, (1 << 23) // max(1, c.shape[0] * c.shape[1]))
+    for r in range(0, x.shape[0], rows):
+        out[r:r + rows] = ((x[r:r + rows, None, :] - c[None, :, :]) ** 2).sum(axis=-1)
+    return out
 
 
 def ivf_assign(K: np.ndarray, centroids: np.ndarray) -> np.ndarray:
