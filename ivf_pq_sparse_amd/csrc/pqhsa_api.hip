@@ -275,7 +275,7 @@ pqhsa_status run_step(const pqhsa_shape* shape, const void* index_buf, const uin
 }
 
 struct AppendWs {
-  size_t old_off, shift, codes, pos, list, total;
+  size_t old_off, shift, codes, pos, list, best, total;
 };
 
 AppendWs append_ws(const Dims& d) {
@@ -287,6 +287,7 @@ AppendWs append_ws(const Dims& d) {
   w.codes = o;   o = align_up(o + BH * d.cap * kM);
   w.pos = o;     o = align_up(o + BH * d.cap * sizeof(int32_t));
   w.list = o;    o = align_up(o + BH * d.cap * sizeof(int32_t));
+  w.best = o;    o = align_up(o + BH * d.cap * sizeof(unsigned long long));
   w.total = o;
   return w;
 }
@@ -479,6 +480,7 @@ pqhsa_status pqhsa_append_tokens(const pqhsa_shape* shape, void* index_buf,
   aa.snap_codes = reinterpret_cast<uint8_t*>(ws + lw.codes);
   aa.snap_pos = reinterpret_cast<int32_t*>(ws + lw.pos);
   aa.snap_list = reinterpret_cast<int32_t*>(ws + lw.list);
+  aa.best = reinterpret_cast<unsigned long long*>(ws + lw.best);
   // 1. encode the new tokens (reads the index's current n_indexed)
   PQHSA_TRY(hip_status(launch_append_encode(aa, max_new, stream)));
   // 2. snapshot the cluster offsets and the cluster-major arrays

@@ -10,14 +10,20 @@
 //   list = argmin_c ||K_t - C_c||^2, code_m = argmin_j ||r^(m) - B_m[j]||^2,
 //   r = K_t - C[list], lowest index on equal distances, fp32 arithmetic.
 //
-//   k_append_assign  one block per (b, h, 64 new tokens): keys from the paged
-//                    cache and 64-centroid chunks (the next chunk's loads in
-//                    flight) in padded LDS rows; each thread owns a 4 token x
-//                    4 centroid tile of distances, a 16-lane reduction picks
-//                    each key's list.  Writes the token-order list ids.
-//   k_append_pq      one block per (b, h, 64 new tokens) with the codebook in
-//                    LDS: thread (4 tokens, subspace) forms the residual slices
-//                    and scans the subspace's 256 codewords.  Writes the codes.
+//   k_append_assign  one block per (b, h, 64 new tokens, run of centroid
+//                    chunks): keys from the paged cache and 64-centroid chunks
+//                    (the next chunk's loads in flight) in padded LDS rows;
+//                    each thread owns a 4 token x 4 centroid tile of
+//                    distances, a 16-lane reduction picks each key's nearest
+//                    centroid of the run.  Small batches split the centroids
+//                    over several blocks, whose results meet in a 64-bit
+//                    minimum of (distance bits, list) per token.
+//   k_append_pq      one wave per (b, h, 64 new tokens, subspace, quarter of
+//                    the codewords): the wave stages its 64 codewords in LDS
+//                    (one per lane) and each lane scans them, by broadcast
+//                    reads, for its token's residual slice; the block's four
+//                    quarters are merged in LDS.  Writes the codes and the
+//                    list ids.
 //   regroup          new cluster offsets from the new tokens' counts; old
 //                    entries move (from a snapshot) by the number of new
 //                    entries in clusters before theirs; new tokens are placed
@@ -25,6 +31,8 @@
 //   k_append_means   one wave per cluster: the cluster's new entries are the
 //                    last ones of its range (the sort keeps token order), so
 //                    mu' = (n_old mu + sum of their V) / n_new.
+#include <algorithm>
+
 #include "pqhsa_internal.hpp"
 
 namespace pqhsa {
@@ -37,9 +45,7 @@ constexpr int kAsgCents = 64;      // centroids per LDS chunk of the assignment
 // LDS rows of keys and centroids, padded so that 16 consecutive rows read by
 // one 16-lane group start 4 banks apart
 constexpr int kRowPad = kD + 4;
-// codebook rows padded by 4 floats per subspace so that the 16 subspaces read
-// by one wave fall on different LDS banks
-constexpr int kCbStride = kKsub * kDsub + 4;
+constexpr int kPqQuarter = kKsub / 4;   // codewords per wave of the code pass
 
 __device__ __forceinline__ void better(float& d, int& c, float d2, int c2) {
   if (d2 < d || (d2 == d && c2 < c)) { d = d2; c = c2; }
@@ -86,19 +92,22 @@ __global__ __launch_bounds__(kEncThreads) void k_append_assign(AppendArgs a) {
   for (int i = 0; i < 4; ++i) { bd[i] = INFINITY; bc[i] = 0x7fffffff; }
   const float4* cen4 = reinterpret_cast<const float4*>(a.ix.centroids + (size_t)bh * d.L * kD);
   constexpr int kPer = kAsgCents * (kD / 4) / kEncThreads;   // float4 of a chunk per thread
+  // this block's centroids [cb0, cb1)
+  const int cb0 = blockIdx.z * a.asg_chunks * kAsgCents;
+  const int cb1 = min(d.L, cb0 + a.asg_chunks * kAsgCents);
   float4 pre[kPer];
   auto load_chunk = [&](int c0) {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int idx = tid + u * kEncThreads, row = idx / (kD / 4), q = idx % (kD / 4);
-      pre[u] = c0 + row < d.L ? cen4[(size_t)(c0 + row) * (kD / 4) + q]
+      pre[u] = c0 + row < cb1 ? cen4[(size_t)(c0 + row) * (kD / 4) + q]
                               : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  load_chunk(0);
+  load_chunk(cb0);
   const float4* keyl4 = reinterpret_cast<const float4*>(keyl);
   const float4* cenl4 = reinterpret_cast<const float4*>(cenl);
-  for (int c0 = 0; c0 < d.L; c0 += kAsgCents) {
+  for (int c0 = cb0; c0 < cb1; c0 += kAsgCents) {
     __syncthreads();   // the previous chunk is no longer read
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
@@ -106,7 +115,7 @@ __global__ __launch_bounds__(kEncThreads) void k_append_assign(AppendArgs a) {
       reinterpret_cast<float4*>(cenl + row * kRowPad)[q] = pre[u];
     }
     __syncthreads();
-    if (c0 + kAsgCents < d.L) load_chunk(c0 + kAsgCents);
+    if (c0 + kAsgCents < cb1) load_chunk(c0 + kAsgCents);
     float acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -138,7 +147,7 @@ __global__ __launch_bounds__(kEncThreads) void k_append_assign(AppendArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = c0 + cq + 16 * j;
-        if (c < d.L) better(bd[i], bc[i], acc[i][j], c);
+        if (c < cb1) better(bd[i], bc[i], acc[i][j], c);
       }
   }
   // each token's best over the 16 lanes of its row
@@ -155,80 +164,110 @@ __global__ __launch_bounds__(kEncThreads) void k_append_assign(AppendArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tk = tq * 4 + i;
-      if (tk < nt) a.list_ids[(size_t)bh * d.cap + t0 + tk] = min(max(bc[i], 0), d.L - 1);
+      if (tk < nt) {
+        // distances are >= 0, so their bits order like the floats; on equal
+        // distances the lower list wins
+        const unsigned long long v = ((unsigned long long)__float_as_uint(bd[i]) << 32) |
+                                     (uint32_t)min(max(bc[i], 0), d.L - 1);
+        unsigned long long* dst = a.best + (size_t)bh * d.cap + t0 + tk;
+        if (gridDim.z > 1) atomicMin(dst, v);
+        else *dst = v;
+      }
     }
   }
 }
 
-__global__ __launch_bounds__(kEncThreads) void k_append_pq(AppendArgs a) {
-  extern __shared__ __align__(16) float cb[];   // [16][kCbStride]
+// The 64-bit minima start above every candidate when the centroids are split.
+__global__ __launch_bounds__(256) void k_append_best_init(AppendArgs a) {
+  const Dims& d = a.d;
+  const int bh = blockIdx.x;
+  const int b = bh / d.Hkv;
+  const int old_n = min(max(a.ix.n_indexed[b], 0), d.cap);
+  const int new_n = min(max(a.new_n_indexed[b], 0), d.cap);
+  for (int t = old_n + blockIdx.y * blockDim.x + threadIdx.x; t < new_n;
+       t += gridDim.y * blockDim.x)
+    a.best[(size_t)bh * d.cap + t] = ~0ull;
+}
+
+__global__ __launch_bounds__(256) void k_append_pq(AppendArgs a) {
+  __shared__ float4 cbq[4][kPqQuarter][2];   // each wave's codewords
+  __shared__ float qbest[4][64];
+  __shared__ int qcode[4][64];
   const Dims& d = a.d;
   const int bh = blockIdx.x;
   const int b = bh / d.Hkv, h = bh % d.Hkv;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int quarter = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = blockIdx.z;
   const int old_n = min(max(a.ix.n_indexed[b], 0), d.cap);
   const int new_n = min(max(a.new_n_indexed[b], 0), d.cap);
   const int t0 = old_n + blockIdx.y * kEncTokens;
   const int nt = min(kEncTokens, new_n - t0);
   if (nt <= 0) return;
-  // the codebook of this (b, h) into LDS
-  const float* cbg = a.ix.codebooks + (size_t)bh * kM * kKsub * kDsub;
-  for (int i = tid; i < kM * kKsub * kDsub / 4; i += kEncThreads) {
-    const int m = i / (kKsub * kDsub / 4), r = i % (kKsub * kDsub / 4);
-    *reinterpret_cast<float4*>(cb + m * kCbStride + r * 4) =
-        reinterpret_cast<const float4*>(cbg)[i];
+  const int t = t0 + lane;
+  const bool ok = lane < nt;
+  // this wave's quarter of subspace m's codewords, one per lane, into LDS
+  const int j0 = quarter * kPqQuarter;
+  {
+    const float4* cbg = reinterpret_cast<const float4*>(
+        a.ix.codebooks + (((size_t)bh * kM + m) * kKsub + j0 + lane) * kDsub);
+    cbq[quarter][lane][0] = cbg[0];
+    cbq[quarter][lane][1] = cbg[1];
   }
-  // residual slices r^(m) = K_t - C[list_t] of this thread's tokens tq*4 + i
-  const int m = tid % kM, tq = tid / kM;
-  const int32_t* tab = a.table + (size_t)b * d.max_pages;
-  const float* cen = a.ix.centroids + (size_t)bh * d.L * kD;
-  float r[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tk = tq * 4 + i;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) r[i][u] = 0.0f;
-    if (tk < nt) {
-      const int t = t0 + tk;
-      const int list = min(max(a.list_ids[(size_t)bh * d.cap + t], 0), d.L - 1);
-      int page = tab[t >> 4];
-      page = min(max(page, 0), d.num_pages - 1);
-      const uint4 w = *reinterpret_cast<const uint4*>(
-          a.kc + ((size_t)(page * kPage + (t & (kPage - 1))) * d.Hkv + h) * kD + m * kDsub);
-      const float4 c0v = *reinterpret_cast<const float4*>(cen + (size_t)list * kD + m * kDsub);
-      const float4 c1v = *reinterpret_cast<const float4*>(cen + (size_t)list * kD + m * kDsub + 4);
-      r[i][0] = bf16_lo(w.x) - c0v.x; r[i][1] = bf16_hi(w.x) - c0v.y;
-      r[i][2] = bf16_lo(w.y) - c0v.z; r[i][3] = bf16_hi(w.y) - c0v.w;
-      r[i][4] = bf16_lo(w.z) - c1v.x; r[i][5] = bf16_hi(w.z) - c1v.y;
-      r[i][6] = bf16_lo(w.w) - c1v.z; r[i][7] = bf16_hi(w.w) - c1v.w;
-    }
+  // residual slice r^(m) = K_t[m] - C[list_t][m] of this lane's token
+  float r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int list = 0;
+  if (ok) {
+    list = min(max((int)(uint32_t)a.best[(size_t)bh * d.cap + t], 0), d.L - 1);
+    const int32_t* tab = a.table + (size_t)b * d.max_pages;
+    int page = tab[t >> 4];
+    page = min(max(page, 0), d.num_pages - 1);
+    const uint4 w = *reinterpret_cast<const uint4*>(
+        a.kc + ((size_t)(page * kPage + (t & (kPage - 1))) * d.Hkv + h) * kD + m * kDsub);
+    const float* cen = a.ix.centroids + ((size_t)bh * d.L + list) * kD + m * kDsub;
+    const float4 c0v = *reinterpret_cast<const float4*>(cen);
+    const float4 c1v = *reinterpret_cast<const float4*>(cen + 4);
+    r[0] = bf16_lo(w.x) - c0v.x; r[1] = bf16_hi(w.x) - c0v.y;
+    r[2] = bf16_lo(w.y) - c0v.z; r[3] = bf16_hi(w.y) - c0v.w;
+    r[4] = bf16_lo(w.z) - c1v.x; r[5] = bf16_hi(w.z) - c1v.y;
+    r[6] = bf16_lo(w.w) - c1v.z; r[7] = bf16_hi(w.w) - c1v.w;
   }
   __syncthreads();
-  float best[4];
-  int code[4];
+  // every lane scans the same codewords (LDS broadcast reads)
+  float best = INFINITY;
+  int code = j0;
+#pragma unroll 2
+  for (int j = 0; j < kPqQuarter; j += 4) {
+    float4 wv[4][2];   // four codewords read ahead of their use
 #pragma unroll
-  for (int i = 0; i < 4; ++i) { best[i] = INFINITY; code[i] = 0; }
-  const float* cbm = cb + m * kCbStride;
-#pragma unroll 4
-  for (int j = 0; j < kKsub; ++j) {
-    const float4 w0 = *reinterpret_cast<const float4*>(cbm + j * kDsub);
-    const float4 w1 = *reinterpret_cast<const float4*>(cbm + j * kDsub + 4);
-    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    for (int k = 0; k < 4; ++k) {
+      wv[k][0] = cbq[quarter][j + k][0];
+      wv[k][1] = cbq[quarter][j + k][1];
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float e = r[i][0] - wv[0], acc = e * e;
+    for (int k = 0; k < 4; ++k) {
+      const float w[8] = {wv[k][0].x, wv[k][0].y, wv[k][0].z, wv[k][0].w,
+                          wv[k][1].x, wv[k][1].y, wv[k][1].z, wv[k][1].w};
+      float e = r[0] - w[0], acc = e * e;
 #pragma unroll
-      for (int u = 1; u < 8; ++u) {
-        e = r[i][u] - wv[u];
+      for (int u = 1; u < kDsub; ++u) {
+        e = r[u] - w[u];
         acc = fmaf(e, e, acc);
       }
-      if (acc < best[i]) { best[i] = acc; code[i] = j; }
+      if (acc < best) { best = acc; code = j0 + j + k; }
     }
   }
+  qbest[quarter][lane] = best;
+  qcode[quarter][lane] = code;
+  __syncthreads();
+  if (quarter == 0 && ok) {
+    // quarters in codeword order: a strictly smaller distance wins, so the
+    // lowest codeword stays on ties
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tk = tq * 4 + i;
-    if (tk < nt) a.codes[((size_t)bh * d.cap + t0 + tk) * kM + m] = (uint8_t)code[i];
+    for (int q = 1; q < 4; ++q)
+      if (qbest[q][lane] < best) { best = qbest[q][lane]; code = qcode[q][lane]; }
+    a.codes[((size_t)bh * d.cap + t) * kM + m] = (uint8_t)code;
+    if (m == 0) a.list_ids[(size_t)bh * d.cap + t] = list;
   }
 }
 
@@ -340,9 +379,6 @@ __global__ __launch_bounds__(256) void k_append_move(AppendArgs a) {
   a.ix.ent_list[base + dst] = c;
 }
 
-// One wave per (b, h): the new tokens in token order, each after the old
-// entries of its cluster and the earlier new ones (rank inside a 64-token
-// tile by comparing list ids, running counts per cluster in LDS).
 // Place the new tokens of one (b, h) after their clusters' old entries, in
 // token order, kPlaceTile tokens at a time.  The tile's list ids go to LDS;
 // W waves each take a contiguous chunk of it and count its tokens per cluster;
@@ -461,12 +497,17 @@ hipError_t launch_append_encode(const AppendArgs& a, int max_new, hipStream_t st
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_append_assign),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)alds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_append_assign, dim3(BH, tiles), dim3(kEncThreads), alds, st, a);
-  const size_t plds = (size_t)kM * kCbStride * sizeof(float);
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_append_pq),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_append_pq, dim3(BH, tiles), dim3(kEncThreads), plds, st, a);
+  // small batches split the centroid chunks over blocks until about 512
+  // blocks run (two per CU fit in LDS)
+  AppendArgs x = a;
+  const int nch = (a.d.L + kAsgCents - 1) / kAsgCents;
+  const int want = std::max(1, std::min(nch, (512 + BH * tiles - 1) / (BH * tiles)));
+  x.asg_chunks = (nch + want - 1) / want;
+  const int splits = (nch + x.asg_chunks - 1) / x.asg_chunks;
+  if (splits > 1)
+    hipLaunchKernelGGL(k_append_best_init, dim3(BH, std::min(tiles, 64)), dim3(256), 0, st, x);
+  hipLaunchKernelGGL(k_append_assign, dim3(BH, tiles, splits), dim3(kEncThreads), alds, st, x);
+  hipLaunchKernelGGL(k_append_pq, dim3(BH, tiles, kM), dim3(256), 0, st, x);
   return hipGetLastError();
 }
 

@@ -156,6 +156,10 @@ struct AppendArgs {
   const uint8_t* snap_codes;     // [BH][cap][16] index arrays before the append
   const int32_t* snap_pos;       // [BH][cap]
   const int32_t* snap_list;      // [BH][cap]
+  // [BH][cap] token order: (fp32 bits of the distance << 32) | list of the
+  // nearest centroid found so far; the minimum over centroid splits
+  unsigned long long* best;
+  int asg_chunks;                // 64-centroid chunks per assignment block
 };
 
 // ---------------------------------------------------------------- device helpers
