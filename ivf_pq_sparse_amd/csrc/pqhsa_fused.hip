@@ -630,24 +630,32 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   };
   if (any) {
     for (int cb = E0; cb < E1; cb += kChunk) {
-      uint32_t chosen = 0;   // bit u: entry u of this thread is above or in the bucket
+      // bit u: entry u of this thread is above (A) or in (T) the bucket
+      uint32_t chosenA = 0, chosenT = 0;
       int ca = 0, ct = 0;
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
-        const int e = cb + u * NT + tid;
-        const uint32_t kv = cb == E0 ? pk[u] : (e < E1 ? keys[e] : 0u);
+        const uint32_t kv = pk[u];
         const int bucket = (int)(kv >> (32 - kHistBits));
-        ca += kv != 0u && bucket > beta;
-        ct += kv != 0u && bucket == beta;
-        if (kv != 0u && bucket >= beta) chosen |= 1u << u;
+        if (kv != 0u && bucket > beta) { ++ca; chosenA |= 1u << u; }
+        if (kv != 0u && bucket == beta) { ++ct; chosenT |= 1u << u; }
+      }
+      // the next chunk's keys load while this chunk is listed and recorded
+      if (cb + kChunk < E1) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          const int e = cb + kChunk + u * NT + tid;
+          pk[u] = e < E1 ? keys[e] : 0u;
+        }
       }
       int oa, ot, ta, tt;
       block_scan2<NT>(ca, ct, &oa, &ot, &ta, &tt, S.sh);
+      uint32_t chosen = chosenA | chosenT;
       while (chosen) {
         const int u = __ffs(chosen) - 1;
         chosen &= chosen - 1;
         const int e = cb + u * NT + tid;
-        const bool isA = (int)(keys[e] >> (32 - kHistBits)) > beta;
+        const bool isA = (chosenA >> u) & 1u;
         const int li = isA ? oa++ : ta + ot++;
         if (li < kListCap) elist[li] = e;
         else record(e, isA, isA ? na + li : nt + li - ta);
