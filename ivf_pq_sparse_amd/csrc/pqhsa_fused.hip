@@ -605,12 +605,16 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   };
   // The block's entries in chunks of NT*16 (entry cb + u*NT + tid to thread
   // tid): count, one block scan, list the chosen entries in LDS (above ones
-  // first, each group in thread order), then record them one list entry per
-  // thread.  Entries beyond the list's capacity are recorded by their thread.
+  // from the front, ties from the back, each group in thread order).  The
+  // list is recorded, one entry per thread, once it would overflow and after
+  // the last chunk, so that the records' gathers of a many-chunk block wait
+  // on memory once.  A chunk larger than the whole list records its entries
+  // by their own threads.
   constexpr int kChunk = NT * kPer;
   constexpr int kListCap = (int)(C::kHBytes / sizeof(int));
   int* elist = reinterpret_cast<int*>(hist);
-  int na = 0, nt = 0;
+  int na = 0, nt = 0;   // records made or listed, above / tie
+  int la = 0, lt = 0;   // of which listed and not yet recorded
   auto record = [&](int e, bool isA, int idx) {
     const int cl = min(max(ent_list[e], c0), c1 - 1);
     const int p = pos[e];
@@ -628,7 +632,47 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       ftc[slot] = cl;
     }
   };
-  if (any) {
+  auto record_list = [&]() {
+    __syncthreads();
+    for (int li = tid; li < la + lt; li += NT) {
+      const bool isA = li < la;
+      if (isA) record(elist[li], true, na - la + li);
+      else record(elist[kListCap - 1 - (li - la)], false, nt - lt + (li - la));
+    }
+    la = lt = 0;
+    __syncthreads();
+  };
+  if (any && E1 - E0 <= kChunk) {
+    // one chunk (the keys already in pk): list, then record
+    int ca = 0, ct = 0;
+    uint32_t chosenA = 0, chosenT = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t kv = pk[u];
+      const int bucket = (int)(kv >> (32 - kHistBits));
+      if (kv != 0u && bucket > beta) { ++ca; chosenA |= 1u << u; }
+      if (kv != 0u && bucket == beta) { ++ct; chosenT |= 1u << u; }
+    }
+    int oa, ot, ta, tt;
+    block_scan2<NT>(ca, ct, &oa, &ot, &ta, &tt, S.sh);
+    uint32_t chosen = chosenA | chosenT;
+    while (chosen) {
+      const int u = __ffs(chosen) - 1;
+      chosen &= chosen - 1;
+      const int e = E0 + u * NT + tid;
+      const bool isA = (chosenA >> u) & 1u;
+      const int li = isA ? oa++ : ta + ot++;
+      if (li < kListCap) elist[li] = e;
+      else record(e, isA, isA ? li : li - ta);
+    }
+    __syncthreads();
+    for (int li = tid; li < min(ta + tt, kListCap); li += NT) {
+      const bool isA = li < ta;
+      record(elist[li], isA, isA ? li : li - ta);
+    }
+    na = ta;
+    nt = tt;
+  } else if (any) {
     for (int cb = E0; cb < E1; cb += kChunk) {
       // bit u: entry u of this thread is above (A) or in (T) the bucket
       uint32_t chosenA = 0, chosenT = 0;
@@ -640,7 +684,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
         if (kv != 0u && bucket > beta) { ++ca; chosenA |= 1u << u; }
         if (kv != 0u && bucket == beta) { ++ct; chosenT |= 1u << u; }
       }
-      // the next chunk's keys load while this chunk is listed and recorded
+      // the next chunk's keys load while this chunk is listed
       if (cb + kChunk < E1) {
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
@@ -650,25 +694,23 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       }
       int oa, ot, ta, tt;
       block_scan2<NT>(ca, ct, &oa, &ot, &ta, &tt, S.sh);
+      const bool fits = ta + tt <= kListCap;
+      if (fits && la + lt + ta + tt > kListCap) record_list();
       uint32_t chosen = chosenA | chosenT;
       while (chosen) {
         const int u = __ffs(chosen) - 1;
         chosen &= chosen - 1;
         const int e = cb + u * NT + tid;
         const bool isA = (chosenA >> u) & 1u;
-        const int li = isA ? oa++ : ta + ot++;
-        if (li < kListCap) elist[li] = e;
-        else record(e, isA, isA ? na + li : nt + li - ta);
-      }
-      __syncthreads();
-      for (int li = tid; li < min(ta + tt, kListCap); li += NT) {
-        const bool isA = li < ta;
-        record(elist[li], isA, isA ? na + li : nt + li - ta);
+        if (!fits) record(e, isA, isA ? na + oa++ : nt + ot++);
+        else if (isA) elist[la + oa++] = e;
+        else elist[kListCap - 1 - (lt + ot++)] = e;
       }
       na += ta;
       nt += tt;
-      __syncthreads();
+      if (fits) { la += ta; lt += tt; }
     }
+    if (la + lt > 0) record_list();
   }
   if (tid == 0)
     st_dev(&a.ws.fcnt[(size_t)bh * kMaxFusedP + sub],

@@ -316,3 +316,16 @@ def test_full_budget_long_context_few_clusters():
     g = run_gpu(inp)
     check_output(g["O"], oracle.dense_step(inp), "budget 100% at 64K vs dense")
     parity(inp, what="budget 100 % at 64K, 8 clusters")
+
+
+@pytest.mark.parametrize("budget_bp", [2500, 6000])
+def test_many_key_chunks_per_block(budget_bp):
+    # 2 clusters over 64K tokens: 2 blocks of 32K entries, four key chunks
+    # each.  At 25 % the chosen entries of two or three chunks fill the
+    # block's list, which a later chunk records before listing its own; at
+    # 60 % every chunk chooses more than the list holds and records its own
+    # entries
+    inp = make_step_inputs(0, context_lens=[65536], num_lists=2, budget_bp=budget_bp,
+                           workload_id=18)
+    log(f"[pqhsa] budget {budget_bp} bp at 64K over 2 clusters")
+    parity(inp, what=f"budget {budget_bp} bp at 64K, 2 clusters")
