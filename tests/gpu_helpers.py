@@ -135,8 +135,12 @@ def parity(inp, heads=None, what="", max_context=None, page_seed=0, staged=False
     rows = [(b, h * G + gg) for b, h in todo for gg in range(G)]
     bi = np.array([r[0] for r in rows]); qi = np.array([r[1] for r in rows])
     mx, l1 = check_output(g["O"][bi, qi], again["O"][bi, qi], what)
-    lse_ref = again["m"] + np.log(again["denom"])
-    lse_err = np.abs(g["lse"][bi, qi] - lse_ref[bi, qi]).max()
+    with np.errstate(divide="ignore"):
+        lse_ref = again["m"] + np.log(again["denom"])
+    gl, rl = g["lse"][bi, qi], lse_ref[bi, qi]
+    # an empty sequence has lse = -inf on both sides
+    both_empty = np.isneginf(gl) & np.isneginf(rl)
+    lse_err = np.where(both_empty, 0.0, np.abs(gl - rl)).max()
     assert lse_err <= LSE_ATOL, f"{what}: lse error {lse_err:.3e}"
     log(f"[parity] {what}: ok max-abs={mx:.2e} l1={l1:.2e} lse={lse_err:.2e} near-tie diffs={nd}")
     return g, ref, again

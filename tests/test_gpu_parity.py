@@ -145,6 +145,16 @@ def test_everything_forced_and_nothing_indexed():
     assert g["selected"][(0, 0)].size == 0
 
 
+def test_empty_and_one_token_sequences():
+    # a sequence of length 0 attends to nothing (O = 0, lse = -inf); one of
+    # length 1 attends to its only token
+    inp = make_step_inputs(1, context_lens=[0, 1, 300], batch=3, num_q_heads=4, num_kv_heads=1,
+                           num_lists=8, n_tail=0, budget_bp=500, workload_id=16)
+    g, _, _ = parity(inp, what="lengths 0, 1 and 300")
+    assert np.all(g["O"][0] == 0.0) and np.all(np.isneginf(g["lse"][0]))
+    assert g["selected"][(0, 0)].size == 0 and g["selected"][(1, 0)].size == 0
+
+
 def test_gqa_group_sizes():
     for G, Hkv in [(1, 4), (2, 2), (8, 1)]:
         inp = make_step_inputs(1, context_lens=[6000], num_q_heads=G * Hkv, num_kv_heads=Hkv,
