@@ -79,9 +79,13 @@ Dims make_dims(const pqhsa_shape* s, bool dense) {
   d.collect_slices = ceil_div(d.cap, kCollectEntries);
   d.upload_chunks = ceil_div(d.cap, kUploadChunk);
   if (dense) {
-    // at least 512 rows per split, and at most 1024 partials per query head
-    const int rows = std::max(kDenseRowsPerSplit, ceil_div(d.cap, 1024));
-    d.n_exact_splits = ceil_div(d.cap, rows);
+    // about two blocks per CU in all (a multiple of 8 splits per (b, h), so
+    // that a head's blocks share an XCD), at least kDenseMinRows rows per
+    // split and at most 1024 partials per query head
+    const int BH = d.B * d.Hkv;
+    int splits = (ceil_div(kDenseBlocks, BH) + 7) / 8 * 8;
+    splits = std::min(splits, std::max(1, ceil_div(d.cap, kDenseMinRows)));
+    d.n_exact_splits = std::max(1, std::min(splits, 1024));
     d.n_bg_splits = 0;
   } else {
     const long long rows_est = (long long)s->n_sink + s->n_recent + max_selected(s) + 512;

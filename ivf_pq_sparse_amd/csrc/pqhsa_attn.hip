@@ -214,35 +214,33 @@ __device__ void exact_block(const StepArgs& a, int bh, int split, AttendLds<G>& 
           ((long long)(page * kPage + (p & (kPage - 1))) * d.Hkv + h) * kD;
     }
     __syncthreads();
+    // rows j and j + 16 of the group per pair; two pairs' buffers alternate
+    // (the loop is unrolled by two so that no buffer is copied), the next
+    // pair's loads in flight while a pair is computed.  A row past the
+    // phase's end loads the phase's last row instead (finite values, weight
+    // zero), so that no register needs clearing.
+    auto load_pair = [&](int j, uint4 (&kv)[4]) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const long long o = sh.row_off[min(j + 16 * r, n - 1)];
+        kv[2 * r] = *reinterpret_cast<const uint4*>(kc + o);
+        kv[2 * r + 1] = *reinterpret_cast<const uint4*>(vc + o);
+      }
+    };
+    auto run_pair = [&](int j, const uint4 (&kv)[4]) {
+      attend_rows2<G>(st, qv, kv[0], kv[1], kv[2], kv[3], act(ph + j),
+                      j + 16 < n ? act(ph + j + 16) : 0u);
+    };
+    uint4 pa[4], pb[4];
     int j = rg;
-    uint4 k0 = make_uint4(0, 0, 0, 0), v0 = k0, k1 = k0, v1 = k0;
-    if (j < n) {
-      const long long o = sh.row_off[j];
-      k0 = *reinterpret_cast<const uint4*>(kc + o);
-      v0 = *reinterpret_cast<const uint4*>(vc + o);
-    }
-    if (j + 16 < n) {
-      const long long o = sh.row_off[j + 16];
-      k1 = *reinterpret_cast<const uint4*>(kc + o);
-      v1 = *reinterpret_cast<const uint4*>(vc + o);
-    }
+    if (j < n) load_pair(j, pa);
     while (j < n) {
-      const int jn = j + 32;
-      uint4 nk0 = k0, nv0 = v0, nk1 = k1, nv1 = v1;
-      if (jn < n) {
-        const long long o = sh.row_off[jn];
-        nk0 = *reinterpret_cast<const uint4*>(kc + o);
-        nv0 = *reinterpret_cast<const uint4*>(vc + o);
-      }
-      if (jn + 16 < n) {
-        const long long o = sh.row_off[jn + 16];
-        nk1 = *reinterpret_cast<const uint4*>(kc + o);
-        nv1 = *reinterpret_cast<const uint4*>(vc + o);
-      }
-      attend_row<G>(st, qv, k0, v0, act(ph + j));
-      if (j + 16 < n) attend_row<G>(st, qv, k1, v1, act(ph + j + 16));
-      k0 = nk0; v0 = nv0; k1 = nk1; v1 = nv1;
-      j = jn;
+      if (j + 32 < n) load_pair(j + 32, pb);
+      run_pair(j, pa);
+      if (j + 32 >= n) break;
+      if (j + 64 < n) load_pair(j + 64, pa);
+      run_pair(j + 32, pb);
+      j += 64;
     }
     __syncthreads();
   }
