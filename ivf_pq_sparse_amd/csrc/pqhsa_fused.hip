@@ -324,7 +324,10 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   // its own cache line: heads and counters do not contend for one line
   uint32_t* sync = a.ws.fsync + (size_t)bh * 3 * kSyncStride;
   uint32_t* ghist = a.ws.hist + (size_t)bh * kHistBins;
-  uint32_t* keys = a.ws.keys + (size_t)bh * d.cap;
+  // the top 16 bits of each entry's selection key (0: not a candidate),
+  // enough for the 12-bit buckets; a tie's full key is recomputed from its
+  // codes when it is recorded
+  uint16_t* keys = reinterpret_cast<uint16_t*>(a.ws.keys) + (size_t)bh * d.cap;
   float* qcg = a.ws.qc + (size_t)bh * d.L * G;
   const uint4* codes = reinterpret_cast<const uint4*>(a.ix.codes + (size_t)bh * d.cap * kM);
   const int32_t* pos = a.ix.pos + (size_t)bh * d.cap;
@@ -507,7 +510,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
 #pragma unroll
           for (int g = 0; g < G; ++g) s[t][g] = v[g];
         }
-        keys[e] = key;
+        keys[e] = (uint16_t)(key >> 16);
       }
     }
 #pragma unroll
@@ -593,12 +596,17 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     __syncthreads();
   }
   const bool any = beta >= 0;
-  auto entry_w = [&](int e, int cl, float* w) {
+  auto entry_w = [&](int e, int cl, float* w, uint32_t* key) {
     const uint4 cw = codes[e];
     float q[G], sv[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) q[g] = qcl[(cl - c0) * G + g];
     entry_logits_lds<G>(lut, q, cw, sv);
+    // the scan's key, bit for bit (same logits, same max order)
+    float kappa = sv[0];
+#pragma unroll
+    for (int g = 1; g < G; ++g) kappa = fmaxf(kappa, sv[g]);
+    *key = order_key(kappa);
 #pragma unroll
     for (int g = 0; g < G; ++g)
       w[g] = __builtin_amdgcn_exp2f(sv[g] - binl[((cl - c0) * G + g) * 2]);
@@ -619,14 +627,15 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     const int cl = min(max(ent_list[e], c0), c1 - 1);
     const int p = pos[e];
     float w[G];
-    entry_w(e, cl, w);
+    uint32_t key;
+    entry_w(e, cl, w, &key);
     if (isA) {
       st_dev(&fpos[E0 + idx], p);
 #pragma unroll
       for (int g = 0; g < G; ++g) atomicAdd(&wsel[(cl - c0) * G + g], to_fixed(w[g]));
     } else {
       const int slot = E0 + idx;
-      st_dev(&ftie[slot], ((unsigned long long)keys[e] << 32) | (uint32_t)p);
+      st_dev(&ftie[slot], ((unsigned long long)key << 32) | (uint32_t)p);
 #pragma unroll
       for (int g = 0; g < G; ++g) ftw[(size_t)slot * G + g] = w[g];
       ftc[slot] = cl;
@@ -649,7 +658,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const uint32_t kv = pk[u];
-      const int bucket = (int)(kv >> (32 - kHistBits));
+      const int bucket = (int)(kv >> (16 - kHistBits));
       if (kv != 0u && bucket > beta) { ++ca; chosenA |= 1u << u; }
       if (kv != 0u && bucket == beta) { ++ct; chosenT |= 1u << u; }
     }
@@ -680,7 +689,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
         const uint32_t kv = pk[u];
-        const int bucket = (int)(kv >> (32 - kHistBits));
+        const int bucket = (int)(kv >> (16 - kHistBits));
         if (kv != 0u && bucket > beta) { ++ca; chosenA |= 1u << u; }
         if (kv != 0u && bucket == beta) { ++ct; chosenT |= 1u << u; }
       }
