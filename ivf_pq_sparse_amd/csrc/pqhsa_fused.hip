@@ -295,7 +295,7 @@ template <int G>
 __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   using C = FusedCfg<G>;
   constexpr int NT = C::NT, NW = C::NW, NG = C::NG;
-  constexpr int PT = 4;   // 64-entry tiles per scan round
+  constexpr int PT = 5;   // 64-entry tiles per scan round (most clusters in one)
   constexpr int kIB = G == 8 ? 2 : 4;  // attention items whose loads are in flight together
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ FusedStatic S;
