@@ -569,21 +569,36 @@ def main():
             pq.decode_step(shape, L_["dec"].index, q, L_["kc"], L_["vc"], L_["bt"], ctx, out, ws)
 
     def timed(dense):
+        """Mean ms per step over the timed steps, and the µs per step of each
+        repetition (one pass over all layer copies) between events recorded
+        on the same stream."""
         for i in range(args.warmup):
             step(i, dense)
         torch.cuda.synchronize()
-        e0, e1 = pq.HipEvent(), pq.HipEvent()
-        e0.record(stream)
+        marks = [pq.HipEvent()]
+        marks[0].record(stream)
         for i in range(args.steps):
             step(i, dense)
-        e1.record(stream)
-        e1.synchronize()
+            if (i + 1) % n_layers == 0 or i + 1 == args.steps:
+                marks.append(pq.HipEvent())
+                marks[-1].record(stream)
+        marks[-1].synchronize()
         torch.cuda.synchronize()
-        return e0.elapsed_ms(e1) / args.steps
+        bounds = [0] + [min(args.steps, (j + 1) * n_layers) for j in range(len(marks) - 1)]
+        per_rep = [marks[j].elapsed_ms(marks[j + 1]) * 1e3 / (bounds[j + 1] - bounds[j])
+                   for j in range(len(marks) - 1) if bounds[j + 1] - bounds[j] == n_layers]
+        return marks[0].elapsed_ms(marks[-1]) / args.steps, per_rep
 
-    ms = timed(False)
+    def spread(per_rep):
+        if not per_rep:
+            return None
+        p = np.percentile(per_rep, [10, 50, 90])
+        return {"p10_us": float(p[0]), "p50_us": float(p[1]), "p90_us": float(p[2]),
+                "reps": len(per_rep), "steps_per_rep": n_layers}
+
+    ms, reps = timed(False)
     log(f"PQ-HSA step: {ms * 1e3:.2f} µs")
-    dense_ms = None if args.no_dense else timed(True)
+    dense_ms, dense_reps = (None, []) if args.no_dense else timed(True)
     if dense_ms is not None:
         log(f"dense split-K step: {dense_ms * 1e3:.2f} µs")
 
@@ -681,7 +696,9 @@ def main():
                    "budget": f"{w['budget_bp'] / 100:g}%", "sink": w["n_sink"],
                    "recent": w["n_recent"], "tail": w["n_tail"], "kv_dtype": "bf16",
                    "page_size": 16, "layer_copies": n_layers},
+        "step_us_spread": spread(reps),
         "dense_us": dense_ms * 1e3 if dense_ms else None,
+        "dense_us_spread": spread(dense_reps),
         "speedup_vs_dense": (dense_ms / ms) if dense_ms else None,
         "step_alg_bytes": step_bytes,
         "step_alg_gbps": step_bytes / (ms * 1e-3) / 1e9,
