@@ -467,7 +467,6 @@ pqhsa_status pqhsa_append_tokens(const pqhsa_shape* shape, void* index_buf,
   if (max_new > d.cap) return PQHSA_ERR_INVALID_ARG;
   const AppendWs lw = append_ws(d);
   if (workspace_bytes < lw.total) return PQHSA_ERR_BUFFER_TOO_SMALL;
-  const size_t BH = (size_t)d.B * d.Hkv;
   char* ws = static_cast<char*>(workspace);
   AppendArgs aa;
   memset(&aa, 0, sizeof(aa));
@@ -485,25 +484,15 @@ pqhsa_status pqhsa_append_tokens(const pqhsa_shape* shape, void* index_buf,
   aa.snap_pos = reinterpret_cast<int32_t*>(ws + lw.pos);
   aa.snap_list = reinterpret_cast<int32_t*>(ws + lw.list);
   aa.best = reinterpret_cast<unsigned long long*>(ws + lw.best);
-  // 1. encode the new tokens (reads the index's current n_indexed)
+  // 1. snapshot the cluster offsets and the cluster-major arrays
+  PQHSA_TRY(hip_status(launch_append_snapshot(aa, stream)));
+  // 2. encode the new tokens (reads the index's current n_indexed)
   PQHSA_TRY(hip_status(launch_append_encode(aa, max_new, stream)));
-  // 2. snapshot the cluster offsets and the cluster-major arrays
-  PQHSA_TRY(hip_status(hipMemcpyAsync(ws + lw.old_off, aa.ix.list_off,
-                                      BH * (d.L + 1) * sizeof(int32_t), hipMemcpyDeviceToDevice,
-                                      stream)));
-  PQHSA_TRY(hip_status(hipMemcpyAsync(ws + lw.codes, aa.ix.codes, BH * d.cap * kM,
-                                      hipMemcpyDeviceToDevice, stream)));
-  PQHSA_TRY(hip_status(hipMemcpyAsync(ws + lw.pos, aa.ix.pos, BH * d.cap * sizeof(int32_t),
-                                      hipMemcpyDeviceToDevice, stream)));
-  PQHSA_TRY(hip_status(hipMemcpyAsync(ws + lw.list, aa.ix.ent_list, BH * d.cap * sizeof(int32_t),
-                                      hipMemcpyDeviceToDevice, stream)));
-  // 3. new offsets, old entries moved, new entries placed
+  // 3. new offsets, new entries placed, old entries moved
   PQHSA_TRY(hip_status(launch_append_regroup(aa, stream)));
-  // 4. fold the new tokens' values into the cluster means
-  PQHSA_TRY(hip_status(launch_append_means(aa, stream)));
-  // 5. the index now covers the new tokens
-  return hip_status(hipMemcpyAsync(aa.ix.n_indexed, new_n_indexed, d.B * sizeof(int32_t),
-                                   hipMemcpyDeviceToDevice, stream));
+  // 4. fold the new tokens' values into the cluster means; the index now
+  //    covers the new tokens
+  return hip_status(launch_append_means(aa, stream));
 }
 
 pqhsa_status pqhsa_index_dropped(const pqhsa_shape* shape, const void* index_buf,

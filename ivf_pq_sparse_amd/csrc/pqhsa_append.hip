@@ -24,10 +24,13 @@
 //                    reads, for its token's residual slice; the block's four
 //                    quarters are merged in LDS.  Writes the codes and the
 //                    list ids.
-//   regroup          new cluster offsets from the new tokens' counts; old
-//                    entries move (from a snapshot) by the number of new
-//                    entries in clusters before theirs; new tokens are placed
-//                    after their cluster's old entries, in token order.
+//   k_append_snapshot the cluster offsets and the held entries' codes,
+//                    positions and clusters copied to the workspace first.
+//   regroup          new cluster offsets from the new tokens' counts, and the
+//                    new tokens placed after their cluster's old entries, in
+//                    token order (k_append_place); then the old entries move
+//                    (from the snapshot) by the number of new entries in
+//                    clusters before theirs (k_append_move).
 //   k_append_means   one wave per cluster: the cluster's new entries are the
 //                    last ones of its range (the sort keeps token order), so
 //                    mu' = (n_old mu + sum of their V) / n_new.
@@ -177,16 +180,27 @@ __global__ __launch_bounds__(kEncThreads) void k_append_assign(AppendArgs a) {
   }
 }
 
-// The 64-bit minima start above every candidate when the centroids are split.
-__global__ __launch_bounds__(256) void k_append_best_init(AppendArgs a) {
+// Before anything moves: the cluster offsets and, for the entries the index
+// holds, their codes, positions and clusters go to the workspace; the new
+// tokens' 64-bit minima start above every candidate.  grid (cap/256, BH).
+__global__ __launch_bounds__(256) void k_append_snapshot(AppendArgs a) {
   const Dims& d = a.d;
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.y;
   const int b = bh / d.Hkv;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  const int32_t* off = a.ix.list_off + (size_t)bh * (d.L + 1);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= d.L; i += blockDim.x) a.old_off[(size_t)bh * (d.L + 1) + i] = off[i];
+  const size_t base = (size_t)bh * d.cap;
+  if (e < min(max(off[d.L], 0), d.cap)) {
+    reinterpret_cast<uint4*>(a.snap_codes)[base + e] =
+        reinterpret_cast<const uint4*>(a.ix.codes)[base + e];
+    a.snap_pos[base + e] = a.ix.pos[base + e];
+    a.snap_list[base + e] = a.ix.ent_list[base + e];
+  }
   const int old_n = min(max(a.ix.n_indexed[b], 0), d.cap);
   const int new_n = min(max(a.new_n_indexed[b], 0), d.cap);
-  for (int t = old_n + blockIdx.y * blockDim.x + threadIdx.x; t < new_n;
-       t += gridDim.y * blockDim.x)
-    a.best[(size_t)bh * d.cap + t] = ~0ull;
+  if (e >= old_n && e < new_n) a.best[base + e] = ~0ull;
 }
 
 __global__ __launch_bounds__(256) void k_append_pq(AppendArgs a) {
@@ -281,6 +295,9 @@ __global__ __launch_bounds__(256) void k_append_means(AppendArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = lane >> 4, l16 = lane & 15;
   const int c = blockIdx.y * 4 + wave;
+  // the index now covers the new tokens (nothing in this kernel reads it)
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < d.B; i += blockDim.x) a.ix.n_indexed[i] = a.new_n_indexed[i];
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int n_old = 0, n_new = 0;
   if (c < d.L) {
@@ -316,52 +333,6 @@ __global__ __launch_bounds__(256) void k_append_means(AppendArgs a) {
   }
 }
 
-// Incremental regroup.  Per (b, h): count the new tokens per cluster, new
-// offsets off'[c] = off[c] + (new tokens in clusters < c); old entries move
-// from a snapshot of the index arrays to off'[c] + (their index within c);
-// new tokens go after them in token order.
-__global__ __launch_bounds__(1024) void k_append_offsets(AppendArgs a) {
-  extern __shared__ int32_t cnt[];     // [L] new tokens per cluster
-  __shared__ int wsum[16];
-  const Dims& d = a.d;
-  const int bh = blockIdx.x;
-  const int b = bh / d.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  for (int c = tid; c < d.L; c += blockDim.x) cnt[c] = 0;
-  __syncthreads();
-  const int old_n = min(max(a.ix.n_indexed[b], 0), d.cap);
-  const int new_n = min(max(a.new_n_indexed[b], 0), d.cap);
-  const int32_t* lists = a.list_ids + (size_t)bh * d.cap;
-  for (int t = old_n + tid; t < new_n; t += blockDim.x) {
-    const int c = lists[t];
-    if (c >= 0 && c < d.L) atomicAdd(&cnt[c], 1);
-  }
-  __syncthreads();
-  // exclusive prefix over clusters: each thread owns a run of them
-  const int per = (d.L + blockDim.x - 1) / blockDim.x;
-  const int c0 = min(d.L, tid * per), c1 = min(d.L, c0 + per);
-  int mine = 0;
-  for (int c = c0; c < c1; ++c) mine += cnt[c];
-  const int incl = wave_incl_scan(mine);
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  int before = incl - mine;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
-  int32_t* off = a.ix.list_off + (size_t)bh * (d.L + 1);
-  const int32_t* oo = a.old_off + (size_t)bh * (d.L + 1);
-  int32_t* shift = a.shift + (size_t)bh * (d.L + 1);
-  for (int c = c0; c < c1; ++c) {
-    shift[c] = before;
-    off[c] = oo[c] + before;
-    before += cnt[c];
-  }
-  if (tid == blockDim.x - 1) {
-    int tot = 0;
-    for (int w = 0; w < nw; ++w) tot += wsum[w];
-    off[d.L] = oo[d.L] + tot;
-    shift[d.L] = tot;
-  }
-}
 
 // One thread per old entry: move codes, position and cluster to the new slot.
 __global__ __launch_bounds__(256) void k_append_move(AppendArgs a) {
@@ -379,8 +350,12 @@ __global__ __launch_bounds__(256) void k_append_move(AppendArgs a) {
   a.ix.ent_list[base + dst] = c;
 }
 
-// Place the new tokens of one (b, h) after their clusters' old entries, in
-// token order, kPlaceTile tokens at a time.  The tile's list ids go to LDS;
+// Incremental regroup, one block per (b, h).  First the new cluster offsets:
+// the new tokens are counted per cluster, off'[c] = off[c] + (new tokens in
+// clusters before c), and that shift is kept for the move of the old entries
+// (a later kernel, from the snapshot).  Then the new tokens are placed after
+// their clusters' old entries, in token order, kPlaceTile tokens at a time
+// (slots that the old entries never take).  The tile's list ids go to LDS;
 // W waves each take a contiguous chunk of it and count its tokens per cluster;
 // a prefix over the chunks gives every chunk its first slot in each cluster
 // (the cluster's next free slot plus the earlier chunks' tokens); then each
@@ -395,20 +370,54 @@ __host__ __device__ inline int place_chunks(int L) { return min(16, max(1, 32768
 __global__ __launch_bounds__(1024) void k_append_place(AppendArgs a) {
   extern __shared__ int32_t slot[];    // [W][L] chunk counts, then chunk slots; [L] next free
   __shared__ int32_t lid[kPlaceTile];  // a tile's clusters, then their slots (-1: none)
+  __shared__ int wsum[16];
   const Dims& d = a.d;
   const int L = d.L;
   const int W = place_chunks(L);
   int32_t* nextf = slot + (size_t)W * L;
   const int bh = blockIdx.x;
   const int b = bh / d.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int old_n = min(max(a.ix.n_indexed[b], 0), d.cap);
   const int new_n = min(max(a.new_n_indexed[b], 0), d.cap);
   const size_t base = (size_t)bh * d.cap;
-  const int32_t* off = a.ix.list_off + (size_t)bh * (L + 1);
+  int32_t* off = a.ix.list_off + (size_t)bh * (L + 1);
   const int32_t* oo = a.old_off + (size_t)bh * (L + 1);
-  // a cluster's new entries start after its old ones, at its new offset
-  for (int c = tid; c < L; c += blockDim.x) nextf[c] = off[c] + (oo[c + 1] - oo[c]);
+  int32_t* shift = a.shift + (size_t)bh * (L + 1);
+  // new tokens per cluster
+  for (int c = tid; c < L; c += blockDim.x) nextf[c] = 0;
+  __syncthreads();
+  for (int t = old_n + tid; t < new_n; t += blockDim.x) {
+    const int c = a.list_ids[base + t];
+    if (c >= 0 && c < L) atomicAdd(&nextf[c], 1);
+  }
+  __syncthreads();
+  {
+    // exclusive prefix over clusters, each thread a run of them; a cluster's
+    // new entries start after its old ones, at its new offset
+    const int per = (L + blockDim.x - 1) / blockDim.x;
+    const int c0 = min(L, tid * per), c1 = min(L, c0 + per);
+    int mine = 0;
+    for (int c = c0; c < c1; ++c) mine += nextf[c];
+    const int incl = wave_incl_scan(mine);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = incl - mine;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    for (int c = c0; c < c1; ++c) {
+      const int n_new_c = nextf[c];
+      shift[c] = before;
+      off[c] = oo[c] + before;
+      nextf[c] = oo[c] + before + (oo[c + 1] - oo[c]);
+      before += n_new_c;
+    }
+    if (tid == blockDim.x - 1) {
+      int tot = 0;
+      for (int w = 0; w < nw; ++w) tot += wsum[w];
+      off[L] = oo[L] + tot;
+      shift[L] = tot;
+    }
+  }
   for (int s0 = old_n; s0 < new_n; s0 += kPlaceTile) {
     const int n = min(kPlaceTile, new_n - s0);
     const int chunk = (n + W - 1) / W;
@@ -479,13 +488,20 @@ __global__ __launch_bounds__(1024) void k_append_place(AppendArgs a) {
 hipError_t launch_append_regroup(const AppendArgs& a, hipStream_t st) {
   const Dims& d = a.d;
   const int BH = d.B * d.Hkv;
-  hipLaunchKernelGGL(k_append_offsets, dim3(BH), dim3(1024), d.L * sizeof(int32_t), st, a);
-  hipLaunchKernelGGL(k_append_move, dim3((d.cap + 255) / 256, BH), dim3(256), 0, st, a);
+  // the new offsets and the new tokens' slots first; the old entries then
+  // move by the shift that kernel leaves (disjoint slots)
   const size_t plds = (size_t)(place_chunks(d.L) + 1) * d.L * sizeof(int32_t);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_append_place),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_append_place, dim3(BH), dim3(1024), plds, st, a);
+  hipLaunchKernelGGL(k_append_move, dim3((d.cap + 255) / 256, BH), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_snapshot(const AppendArgs& a, hipStream_t st) {
+  const int BH = a.d.B * a.d.Hkv;
+  hipLaunchKernelGGL(k_append_snapshot, dim3((a.d.cap + 255) / 256, BH), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -504,8 +520,6 @@ hipError_t launch_append_encode(const AppendArgs& a, int max_new, hipStream_t st
   const int want = std::max(1, std::min(nch, (512 + BH * tiles - 1) / (BH * tiles)));
   x.asg_chunks = (nch + want - 1) / want;
   const int splits = (nch + x.asg_chunks - 1) / x.asg_chunks;
-  if (splits > 1)
-    hipLaunchKernelGGL(k_append_best_init, dim3(BH, std::min(tiles, 64)), dim3(256), 0, st, x);
   hipLaunchKernelGGL(k_append_assign, dim3(BH, tiles, splits), dim3(kEncThreads), alds, st, x);
   hipLaunchKernelGGL(k_append_pq, dim3(BH, tiles, kM), dim3(256), 0, st, x);
   return hipGetLastError();

@@ -152,11 +152,11 @@ struct AppendArgs {
   const int32_t* new_n_indexed;  // [B]
   int32_t* list_ids;             // [BH][cap] token order (written for the new tokens)
   uint8_t* codes;                // [BH][cap][16] token order (written for the new tokens)
-  const int32_t* old_off;        // [BH][L+1] cluster offsets before the append
+  int32_t* old_off;              // [BH][L+1] cluster offsets before the append
   int32_t* shift;                // [BH][L+1] new tokens in clusters before c
-  const uint8_t* snap_codes;     // [BH][cap][16] index arrays before the append
-  const int32_t* snap_pos;       // [BH][cap]
-  const int32_t* snap_list;      // [BH][cap]
+  uint8_t* snap_codes;           // [BH][cap][16] index arrays before the append
+  int32_t* snap_pos;             // [BH][cap]
+  int32_t* snap_list;            // [BH][cap]
   // [BH][cap] token order: (fp32 bits of the distance << 32) | list of the
   // nearest centroid found so far; the minimum over centroid splits
   unsigned long long* best;
@@ -526,6 +526,7 @@ inline hipError_t launch_kernel(void (*kernel)(A), dim3 grid, dim3 block, size_t
 
 hipError_t launch_upload(const UploadArgs& a, hipStream_t st);
 hipError_t launch_upload_regroup(const UploadArgs& a, hipStream_t st);
+hipError_t launch_append_snapshot(const AppendArgs& a, hipStream_t st);
 hipError_t launch_append_encode(const AppendArgs& a, int max_new, hipStream_t st);
 hipError_t launch_append_means(const AppendArgs& a, hipStream_t st);
 hipError_t launch_append_regroup(const AppendArgs& a, hipStream_t st);
