@@ -596,7 +596,7 @@ def main():
         return {"p10_us": float(p[0]), "p50_us": float(p[1]), "p90_us": float(p[2]),
                 "reps": len(per_rep), "steps_per_rep": n_layers}
 
-    ms, reps = timed(False)
+    ms, step_reps = timed(False)
     log(f"PQ-HSA step: {ms * 1e3:.2f} µs")
     dense_ms, dense_reps = (None, []) if args.no_dense else timed(True)
     if dense_ms is not None:
@@ -696,7 +696,7 @@ def main():
                    "budget": f"{w['budget_bp'] / 100:g}%", "sink": w["n_sink"],
                    "recent": w["n_recent"], "tail": w["n_tail"], "kv_dtype": "bf16",
                    "page_size": 16, "layer_copies": n_layers},
-        "step_us_spread": spread(reps),
+        "step_us_spread": spread(step_reps),
         "dense_us": dense_ms * 1e3 if dense_ms else None,
         "dense_us_spread": spread(dense_reps),
         "speedup_vs_dense": (dense_ms / ms) if dense_ms else None,
