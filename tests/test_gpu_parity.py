@@ -351,3 +351,32 @@ def test_many_key_chunks_per_block(budget_bp):
                            workload_id=18)
     log(f"[pqhsa] budget {budget_bp} bp at 64K over 2 clusters")
     parity(inp, what=f"budget {budget_bp} bp at 64K, 2 clusters")
+
+
+def _random_case(seed):
+    """A seeded random shape: batch, heads, group size, ragged lengths
+    (including empty and one-token sequences), list count, sink, recent
+    window, tail, budget, background on or off, fused or staged path."""
+    rng = np.random.default_rng([seed, 99])
+    B = int(rng.integers(1, 4))
+    Hkv = int(rng.integers(1, 4))
+    G = int(rng.choice([1, 2, 4, 8]))
+    lens = [int(rng.choice([0, 1, int(rng.integers(2, 7000))], p=[0.08, 0.07, 0.85]))
+            for _ in range(B)]
+    lens[0] = max(lens[0], int(rng.integers(1000, 7000)))
+    kw = dict(batch=B, num_q_heads=G * Hkv, num_kv_heads=Hkv,
+              num_lists=int(rng.choice([1, 3, 16, 64, 200, 700])),
+              n_sink=int(rng.integers(0, 20)), n_recent=int(rng.integers(0, 300)),
+              budget_bp=int(rng.choice([0, 1, 50, 100, 250, 1000, 5000, 10000])))
+    tail = int(rng.integers(0, 400))
+    background = bool(rng.random() < 0.75)
+    staged = bool(rng.random() < 0.3)
+    return lens, kw, tail, background, staged
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_match_oracle(seed):
+    lens, kw, tail, background, staged = _random_case(seed)
+    inp = make_step_inputs(1, context_lens=lens, n_tail=tail, workload_id=500 + seed, **kw)
+    parity(inp, what=f"random case {seed}", page_seed=seed, staged=staged,
+           background=background)
