@@ -278,8 +278,9 @@ pqhsa_status pqhsa_decode_step_profiled(const pqhsa_shape* shape, const void* in
  *   flags   uint32: bit 0 set if a barrier wait of the fused step ever timed
  *           out (its results are then not valid)
  * The staged step fills lut, qc, keys, bins, rows, n_rows and partials; the
- * fused step fills qc and bins of every cluster, keys, n_rows, and rows in a
- * per-block order. */
+ * fused step fills qc and bins of every cluster, n_rows, rows in a per-block
+ * order, and at the start of keys the top 16 bits of each key as
+ * uint16 [B*Hkv][max_context]. */
 typedef struct pqhsa_ws_layout {
   size_t lut, qc, keys, bins, rows, n_rows, partials, flags;
   int32_t n_exact_splits, n_bg_splits, n_parts;
