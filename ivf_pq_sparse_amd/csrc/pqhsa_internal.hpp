@@ -350,12 +350,28 @@ __device__ __forceinline__ void lut_add(const float* lut, uint32_t code, float* 
   }
 }
 
-// Same sum as entry_logits (same order: qc, then subspaces 0..15).
+// Same sum as entry_logits (same order: qc, then subspaces 0..15).  For
+// G <= 4 all 16 table reads are issued before the first add, so that a wave
+// keeps 16 LDS reads in flight instead of a few.
 template <int G>
 __device__ __forceinline__ void entry_logits_lds(const float* lut, const float* qc, uint4 cw,
                                                  float* s) {
 #pragma unroll
   for (int g = 0; g < G; ++g) s[g] = qc[g];
+  if constexpr (G == 4) {
+    const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+    float4 v[kM];
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      const uint32_t code = (w[m >> 2] >> ((m & 3) * 8)) & 0xffu;
+      v[m] = *reinterpret_cast<const float4*>(lut + m * kKsub * 4 + code * 4);
+    }
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      s[0] += v[m].x; s[1] += v[m].y; s[2] += v[m].z; s[3] += v[m].w;
+    }
+    return;
+  }
   lut_add<G, 0>(lut, cw.x & 0xffu, s);
   lut_add<G, 1>(lut, (cw.x >> 8) & 0xffu, s);
   lut_add<G, 2>(lut, (cw.x >> 16) & 0xffu, s);
