@@ -1,6 +1,7 @@
 """The oracles against examples worked by hand (tests/golden): every
 expected value there is a rational number or a logarithm derived on paper
-from the output formula of the PQ-HSA page, section A, not from any code."""
+from the rule its fixture cites (the PQ-HSA output formula, the append
+encoder and mean update, the query-reuse merge law), not from any code."""
 import math
 import os
 from fractions import Fraction
