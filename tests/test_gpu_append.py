@@ -64,7 +64,11 @@ def _check_encoding(inp, b, h, t0, t1, lists, codes, stride=1):
 # every 29th token, the placement of all of them
 @pytest.mark.parametrize("G,Hkv,L,tail,T", [(4, 2, 64, 512, 6000), (8, 1, 128, 300, 6000),
                                              (1, 3, 40, 17, 6000), (4, 1, 2000, 9000, 12000),
-                                             (2, 1, 8192, 5000, 9000)])
+                                             (2, 1, 8192, 5000, 9000),
+                                             # one new token; a single list; one token short
+                                             # of and one past a placement tile
+                                             (2, 3, 7, 1, 3000), (4, 1, 1, 100, 2000),
+                                             (8, 2, 33, 4095, 6000), (4, 2, 300, 4097, 8000)])
 def test_append_tail_matches_oracle(G, Hkv, L, tail, T):
     from oracle import pqhsa_append as ap
     from oracle import pqhsa_oracle as orc
