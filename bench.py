@@ -31,6 +31,17 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "µs/decode step/layer @128K, 1% budget; HBM GB/s vs peak; × vs dense split-K"
 
 
+def cpu_model():
+    """The host CPU's model name, or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -661,6 +672,7 @@ def main():
     traffic = prof[kname][1] if prof and kname in prof else None
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                "traffic_gbps": (traffic / (stage_us[dom] * 1e-6) / 1e9) if traffic else None,
                 "kernel": kname, "alg_bytes_per_launch": dom_bytes,
                 "launch_us": float(stage_us[dom]),
                 "traffic_over_alg": (traffic / dom_bytes) if traffic else None}
@@ -682,8 +694,20 @@ def main():
                "cores": max(1, int(round(cpu_s / wall))), "kind": "oracle",
                "sample": f"the full step of this workload ({inp.batch * inp.num_kv_heads} KV heads), "
                          f"{reps} repetitions, numpy float64, input generation and index build excluded",
-               "host_threads_available": os.cpu_count()}
+               "host_threads_available": os.cpu_count(), "cpu_model": cpu_model()}
         log(f"oracle: {cpu['value'] / 1e3:.1f} ms/step on ~{cpu['cores']} cores")
+        # the same with the numerical libraries held to one thread
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(1):
+                t1, reps1 = time.time(), 0
+                while reps1 < 1 or (time.time() - t1 < 5.0 and reps1 < 4):
+                    oracle.decode_step(inp)
+                    reps1 += 1
+                cpu["single_thread_value"] = (time.time() - t1) / reps1 * 1e6
+            log(f"oracle, one thread: {cpu['single_thread_value'] / 1e3:.1f} ms/step")
+        except ImportError:
+            cpu["single_thread_value"] = None
 
     us = ms * 1e3
     rec = {
