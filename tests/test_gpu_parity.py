@@ -380,3 +380,28 @@ def test_random_shapes_match_oracle(seed):
     inp = make_step_inputs(1, context_lens=lens, n_tail=tail, workload_id=500 + seed, **kw)
     parity(inp, what=f"random case {seed}", page_seed=seed, staged=staged,
            background=background)
+
+
+@pytest.mark.parametrize("B,expect_kernels", [(32, 1), (40, 6)])
+def test_many_heads_one_block_each_or_staged(B, expect_kernels):
+    # 32 sequences x 8 KV heads = 256 heads: the fused step runs one block per
+    # head (no other block at its barriers); 40 x 8 = 320 heads exceed what
+    # the device holds at once, so the default path is the staged kernels
+    import ivf_pq_sparse_amd as pq
+    from pqhsa_synth.device import stage
+    lens = [600 + 37 * (b % 7) for b in range(B)]
+    inp = make_step_inputs(1, context_lens=lens, batch=B, num_q_heads=32, num_kv_heads=8,
+                           num_lists=16, n_tail=40, budget_bp=500, workload_id=40 + B)
+    tens, kw = stage(inp, "cuda")
+    shape = pq.make_shape(**kw)
+    dec = pq.PQHSADecoder(shape)
+    dec.upload(tens["centroids"], tens["codebooks"], tens["list_ids"], tens["codes"],
+               tens["n_indexed"], tens["v_cache"], tens["block_table"])
+    out = torch.empty(shape.batch, shape.num_q_heads, 128, device="cuda")
+    evs = [pq.HipEvent() for _ in range(2 * pq.NUM_STAGES)]
+    n = pq.decode_step_profiled(shape, dec.index, tens["q"], tens["k_cache"], tens["v_cache"],
+                                tens["block_table"], tens["context_lens"], out, dec.workspace,
+                                evs)
+    torch.cuda.synchronize()
+    assert n == expect_kernels
+    parity(inp, what=f"{B} sequences x 8 KV heads")
