@@ -405,3 +405,12 @@ def test_many_heads_one_block_each_or_staged(B, expect_kernels):
     torch.cuda.synchronize()
     assert n == expect_kernels
     parity(inp, what=f"{B} sequences x 8 KV heads")
+
+
+def test_largest_list_count():
+    # 16384 lists (the largest the library takes) over 40K tokens: about two
+    # tokens per list, more lists per block than the fused step holds, so the
+    # staged kernels run
+    inp = make_step_inputs(1, context_lens=[40000], num_q_heads=8, num_kv_heads=2,
+                           num_lists=16384, budget_bp=200, workload_id=52)
+    parity(inp, what="16384 lists over 40K tokens")
