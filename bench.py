@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="layer copies (0 = enough to exceed MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-other-workloads", action="store_true",
+                   help="skip the 32K, 16 x 128K and 512K lines beside the main workload")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain device copy of known size (for counter scaling)")
     p.add_argument("--sweep", choices=["configs", "budget", "context", "append", "reuse"],
@@ -86,10 +88,11 @@ def algorithmic_bytes(inp, n_rows_per_head, k_sel, n_parts):
       attend:  512 B K+V + 4 B row id per exact row; per head the means
                (L*512 B), bins and selected weights; writes the partials
       merge:   reads the partials (132*4 B each), writes O (512 B per q head)
-      fused:   the whole step in one kernel: 16 B codes + 4 B position per
-               indexed entry, 512 B K+V + 4 B page-table entry per exact row,
-               per head the codebooks, centroids and means, q and O (its
-               scratch stays in L2 and is not counted)
+      fused:   the whole step in one kernel, so the step total (its scratch
+               stays mostly in L2 and is not counted; its position stream and
+               page-table reads are the layout's, not the method's, and are
+               reported apart as `fused_layout`: 4 B per indexed entry and per
+               exact row instead of the 2 B list id)
     """
     B, Hkv, Hq = inp.batch, inp.num_kv_heads, inp.num_q_heads
     G, L = Hq // Hkv, inp.num_lists
@@ -100,9 +103,12 @@ def algorithmic_bytes(inp, n_rows_per_head, k_sel, n_parts):
     lut, qc, bins = 16 * 256 * G * 4, L * G * 4, L * G * 8
     partials = B * Hq * n_parts * 132 * 4
     rec = 8 + 4 * G
+    total = (n_idx * 18 + rows * 512 + BH * (2 * L * 512 + 16 * 256 * 8 * 4)
+             + B * Hq * 128 * (2 + 4))
     k = {
-        "fused": (n_idx * (16 + 4) + rows * (512 + 4) + BH * (16 * 256 * 8 * 4 + 2 * L * 512)
-                  + B * Hq * (256 + 512)),
+        "fused": total,
+        "fused_layout": (n_idx * (16 + 4) + rows * (512 + 4) + BH * (16 * 256 * 8 * 4 + 2 * L * 512)
+                         + B * Hq * (256 + 512)),
         "tables": B * Hq * 256 + BH * (16 * 256 * 8 * 4 + L * 512 + lut + qc),
         "scan": n_idx * (16 + 4 + 4) + BH * (lut + qc + bins + (L + 1) * 4),
         "collect": n_idx * 4 + BH * 4096 * 4 + ksum * rec,
@@ -110,8 +116,6 @@ def algorithmic_bytes(inp, n_rows_per_head, k_sel, n_parts):
         "attend": rows * (512 + 4) + BH * (L * 512 + 2 * bins) + partials,
         "merge": partials + B * Hq * 512,
     }
-    total = (n_idx * 18 + rows * 512 + BH * (2 * L * 512 + 16 * 256 * 8 * 4)
-             + B * Hq * 128 * (2 + 4))
     return total, k
 
 
@@ -303,6 +307,42 @@ class Rig:
         e1.synchronize()
         torch.cuda.synchronize()
         return e0.elapsed_ms(e1) / steps * 1e3
+
+
+def other_workloads(main_wid, steps=64, warmup=8):
+    """The 32K, 16 x 128K and 512K workloads beside the main one: PQ-HSA and
+    dense split-K µs per step on rotated layer copies, the speed-up and the
+    step's algorithmic bytes and rate."""
+    import torch
+
+    import ivf_pq_sparse_amd as pq
+    from pqhsa_synth import WORKLOADS, make_step_inputs
+    out = {}
+    for wid in (1, 3, 4):
+        if wid == main_wid:
+            continue
+        w = WORKLOADS[wid]
+        t0 = time.time()
+        inp = make_step_inputs(wid)
+        rig = Rig(inp)
+        us = rig.timed(False, steps, warmup)
+        dus = rig.timed(True, steps, warmup)
+        flags = pq.step_flags(rig.shape, rig.ws)
+        if flags:
+            raise SystemExit(f"workload {wid}: a barrier wait of the fused step ran out")
+        k = -(-w["context"] * w["budget_bp"] // 10000)
+        n_rows = np.full(w["batch"] * w["num_kv_heads"],
+                         w["n_sink"] + k + max(w["n_recent"], w["n_tail"]))
+        tot, _ = algorithmic_bytes(inp, n_rows, np.full(n_rows.size, k), 1)
+        out[w["name"]] = {"pqhsa_us": us, "dense_us": dus, "speedup_vs_dense": dus / us,
+                          "step_alg_bytes": tot, "step_alg_gbps": tot / (us * 1e-6) / 1e9,
+                          "dense_gbps": rig.kv_bytes / (dus * 1e-6) / 1e9,
+                          "layer_copies": rig.n_layers, "steps": steps}
+        log(f"workload {wid} ({w['name']}): PQ-HSA {us:.1f} µs, dense {dus:.1f} µs "
+            f"({time.time() - t0:.0f} s)")
+        del rig, inp
+        torch.cuda.empty_cache()
+    return out
 
 
 def reuse_sweep(steps, warmup, window=1024):
@@ -580,36 +620,46 @@ def main():
             pq.decode_step(shape, L_["dec"].index, q, L_["kc"], L_["vc"], L_["bt"], ctx, out, ws)
 
     def timed(dense):
-        """Mean ms per step over the timed steps, and the µs per step of each
-        repetition (one pass over all layer copies) between events recorded
-        on the same stream."""
+        """Mean ms per step over the timed steps (events at both ends only)."""
         for i in range(args.warmup):
             step(i, dense)
         torch.cuda.synchronize()
-        marks = [pq.HipEvent()]
-        marks[0].record(stream)
+        e0, e1 = pq.HipEvent(), pq.HipEvent()
+        e0.record(stream)
         for i in range(args.steps):
             step(i, dense)
-            if (i + 1) % n_layers == 0 or i + 1 == args.steps:
-                marks.append(pq.HipEvent())
-                marks[-1].record(stream)
-        marks[-1].synchronize()
+        e1.record(stream)
+        e1.synchronize()
         torch.cuda.synchronize()
-        bounds = [0] + [min(args.steps, (j + 1) * n_layers) for j in range(len(marks) - 1)]
-        per_rep = [marks[j].elapsed_ms(marks[j + 1]) * 1e3 / (bounds[j + 1] - bounds[j])
-                   for j in range(len(marks) - 1) if bounds[j + 1] - bounds[j] == n_layers]
-        return marks[0].elapsed_ms(marks[-1]) / args.steps, per_rep
+        return e0.elapsed_ms(e1) / args.steps
 
-    def spread(per_rep):
-        if not per_rep:
+    def per_step(dense):
+        """µs of each step of a separate pass (at least 64 steps, at most 256)
+        with an event recorded after every step on the step stream: the spread
+        of single steps, whatever --steps is.  The extra events make each step
+        a little slower than in the timed loop."""
+        n = min(256, max(64, args.steps))
+        marks = [pq.HipEvent() for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        marks[0].record(stream)
+        for i in range(n):
+            step(i, dense)
+            marks[i + 1].record(stream)
+        marks[-1].synchronize()
+        return [marks[i].elapsed_ms(marks[i + 1]) * 1e3 for i in range(n)]
+
+    def spread(per):
+        if not per:
             return None
-        p = np.percentile(per_rep, [10, 50, 90])
+        p = np.percentile(per, [10, 50, 90])
         return {"p10_us": float(p[0]), "p50_us": float(p[1]), "p90_us": float(p[2]),
-                "reps": len(per_rep), "steps_per_rep": n_layers}
+                "steps": len(per), "source": "one event after every step, separate pass"}
 
-    ms, step_reps = timed(False)
+    ms = timed(False)
     log(f"PQ-HSA step: {ms * 1e3:.2f} µs")
-    dense_ms, dense_reps = (None, []) if args.no_dense else timed(True)
+    step_reps = per_step(False)
+    dense_ms = None if args.no_dense else timed(True)
+    dense_reps = [] if args.no_dense else per_step(True)
     if dense_ms is not None:
         log(f"dense split-K step: {dense_ms * 1e3:.2f} µs")
 
@@ -661,8 +711,9 @@ def main():
         log(f"copy calibration: {n * 4} bytes read and written")
 
     # dominant kernel (longest average duration) and its roofline over its
-    # algorithmic bytes; traffic from the committed counter summary when it was
-    # taken on these kernel sources
+    # algorithmic bytes (for the fused kernel, the whole step's: codes, list
+    # ids, exact rows, index tables, q and O); traffic from the committed
+    # counter summary when it was taken on these kernel sources
     dom = int(np.argmax(stage_us))
     dom_bytes = kbytes[names[dom]]
     achieved = dom_bytes / (stage_us[dom] * 1e-6) / 1e9
@@ -676,6 +727,11 @@ def main():
                 "kernel": kname, "alg_bytes_per_launch": dom_bytes,
                 "launch_us": float(stage_us[dom]),
                 "traffic_over_alg": (traffic / dom_bytes) if traffic else None}
+    if fused:
+        # the layout's own bytes (4 B positions, page-table entries) beside
+        roofline["layout_bytes_per_launch"] = kbytes["fused_layout"]
+        roofline["frac_over_layout_bytes"] = (kbytes["fused_layout"] / (stage_us[dom] * 1e-6)
+                                              / 1e9 / HBM_PEAK_GBS)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -709,6 +765,12 @@ def main():
         except ImportError:
             cpu["single_thread_value"] = None
 
+    others = None
+    if not args.no_other_workloads:
+        del layers, ws, dense_ws
+        torch.cuda.empty_cache()
+        others = other_workloads(args.workload)
+
     us = ms * 1e3
     rec = {
         "metric": METRIC, "value": us, "unit": "µs/step/layer", "n_gpus": 1, "steps": args.steps,
@@ -734,6 +796,7 @@ def main():
                              if dense_stage is not None else None),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "other_workloads": others,
     }
     print(json.dumps(rec), flush=True)
 

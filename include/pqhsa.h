@@ -145,7 +145,10 @@ size_t pqhsa_append_workspace_bytes(const pqhsa_shape* shape);
  *   new_n_indexed  int32 [B] device; new_n_indexed[b] >= the index's current
  *                  n_indexed[b] and <= max_context
  *   max_new        host bound on new_n_indexed[b] - n_indexed[b] over b
- *                  (sizes the grid; tokens beyond it are not encoded)
+ *                  (sizes the grid).  At most max_new tokens of a sequence
+ *                  are added: its n_indexed becomes
+ *                  min(new_n_indexed[b], n_indexed_b + max_new), and any
+ *                  further tokens stay in the exact tail.
  *   list_ids       int32 [B][Hkv][max_context], the token-order list ids the
  *                  index was uploaded from; entries of the new tokens are
  *                  written, all indexed entries are read
@@ -205,9 +208,13 @@ pqhsa_status pqhsa_index_dropped(const pqhsa_shape* shape, const void* index_buf
  * below (staged step).  Both compute the same quantities.  The fused step
  * assumes its blocks can all be resident together: on a device whose CUs are
  * partly withheld (CU masking, long-running concurrent kernels) a barrier wait
- * may time out after about 2 s, which sets bit 0 of the workspace flags
- * (pqhsa_workspace_layout) and leaves that step's results invalid; the staged
- * variant of pqhsa_decode_step_profiled has no such requirement. */
+ * may run out after about 2 s.  The call still returns PQHSA_OK (it cannot
+ * wait for the device), the affected KV head's `out` and `lse` entries are NaN,
+ * and bit 0 of the workspace flags is set.  Checking that flag with
+ * pqhsa_step_flags is the caller's duty wherever CUs may be withheld; once it
+ * is set, the workspace must be cleared (pqhsa_step_flags with clear != 0)
+ * before the next step.  The staged variant of pqhsa_decode_step_profiled has
+ * no residency requirement. */
 pqhsa_status pqhsa_decode_step(const pqhsa_shape* shape, const void* index_buf,
                                const uint16_t* q, const uint16_t* k_cache,
                                const uint16_t* v_cache, const int32_t* block_table,
@@ -246,7 +253,14 @@ enum {
 enum {
   PQHSA_VARIANT_DEFAULT = 0,  /* exactly what pqhsa_decode_step runs */
   PQHSA_VARIANT_STAGED = 1,   /* the six staged kernels, whatever the shape */
-  PQHSA_VARIANT_DENSE = 2     /* pqhsa_dense_decode_step (index_buf unused) */
+  PQHSA_VARIANT_DENSE = 2,    /* pqhsa_dense_decode_step (index_buf unused) */
+  PQHSA_VARIANT_BARRIER_TEST = 3  /* test only: the fused step with barriers that
+                                     wait for one block more than there are and
+                                     give up after 20 us, so that every wait runs
+                                     out (every kernel still ends normally): all
+                                     outputs NaN, flags bit 0 set.  Returns
+                                     PQHSA_ERR_UNSUPPORTED where the fused step
+                                     cannot run the shape. */
 };
 
 /* A decode step that also times its kernels.  events holds 2 * PQHSA_NUM_STAGES
@@ -281,11 +295,27 @@ pqhsa_status pqhsa_decode_step_profiled(const pqhsa_shape* shape, const void* in
  * fused step fills qc and bins of every cluster, n_rows, rows in a per-block
  * order, and at the start of keys the top 16 bits of each key as
  * uint16 [B*Hkv][max_context]. */
+/* Also: hist (uint32 [B*Hkv][4096] key histogram, hist_bytes long) and
+ * counters (the fused step's per-head barrier counters and flags, the flags
+ * word and per-block counts, counters_bytes long): the regions a step expects
+ * to find cleared; total = pqhsa_workspace_bytes. */
 typedef struct pqhsa_ws_layout {
   size_t lut, qc, keys, bins, rows, n_rows, partials, flags;
   int32_t n_exact_splits, n_bg_splits, n_parts;
+  size_t hist, hist_bytes, counters, counters_bytes, total;
 } pqhsa_ws_layout;
 pqhsa_status pqhsa_workspace_layout(const pqhsa_shape* shape, int dense, pqhsa_ws_layout* out);
+
+/* Status word of a decode-step workspace: *flags gets the flags word (bit 0:
+ * a barrier wait of the fused step ran out since the workspace was last
+ * cleared, so the outputs of the heads involved were written as NaN).  With
+ * clear != 0 the workspace's counters, flags and histogram are then zeroed,
+ * which makes it ready for the next step.  Synchronises `stream` (meant for
+ * error handling and tests, not for every step).  Errors: shape errors as in
+ * pqhsa_decode_step; PQHSA_ERR_INVALID_ARG for a NULL pointer;
+ * PQHSA_ERR_BUFFER_TOO_SMALL for a short workspace; PQHSA_ERR_HIP. */
+pqhsa_status pqhsa_step_flags(const pqhsa_shape* shape, void* workspace, size_t workspace_bytes,
+                              int clear, uint32_t* flags, hipStream_t stream);
 
 /* Byte offsets of the index arrays inside index_buf (bh = b * Hkv + h):
  *   centroids float [B*Hkv][L][128], codebooks float [B*Hkv][16][256][8],

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     append_tokens,
     append_workspace_bytes,
     NUM_STAGES,
+    VARIANT_BARRIER_TEST,
     VARIANT_DEFAULT,
     VARIANT_DENSE,
     VARIANT_STAGED,
@@ -38,6 +39,7 @@ from ._lib import (  # noqa: F401
     reuse_decode_step,
     reuse_layout,
     reuse_workspace_bytes,
+    step_flags,
     status_string,
     upload_index,
     upload_workspace_bytes,
@@ -110,11 +112,11 @@ class PQHSADecoder:
                         self.workspace, selected=sel, lse=ls, stream=stream)
         return out, sel, ls
 
-    def flags(self) -> int:
-        """The workspace's status word (bit 0: a fused-step barrier wait timed
-        out).  Synchronises with the device through the copy."""
-        off = workspace_layout(self.shape).flags
-        return int(self.workspace[off:off + 4].view(torch.int32).item())
+    def flags(self, clear: bool = False) -> int:
+        """The workspace's status word (bit 0: a fused-step barrier wait ran
+        out), through pqhsa_step_flags; clear=True also readies the workspace
+        for the next step.  Synchronises the current stream."""
+        return step_flags(self.shape, self.workspace, clear=clear)
 
     def dense_workspace(self):
         if self._dense_ws is None:

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libpqhsa.so")
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "buffer too small",
           4: "HIP error"}
 NUM_STAGES = 6
-VARIANT_DEFAULT, VARIANT_STAGED, VARIANT_DENSE = 0, 1, 2
+VARIANT_DEFAULT, VARIANT_STAGED, VARIANT_DENSE, VARIANT_BARRIER_TEST = 0, 1, 2, 3
 STAGE_NAMES = ["tables", "scan", "collect", "select", "attend", "merge"]
 
 
@@ -42,7 +42,9 @@ class Shape(ctypes.Structure):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "lut", "qc", "keys", "bins", "rows", "n_rows", "partials", "flags")] + [
-        (n, ctypes.c_int32) for n in ("n_exact_splits", "n_bg_splits", "n_parts")]
+        (n, ctypes.c_int32) for n in ("n_exact_splits", "n_bg_splits", "n_parts")] + [
+        (n, ctypes.c_size_t) for n in ("hist", "hist_bytes", "counters", "counters_bytes",
+                                       "total")]
 
 
 class ReuseLayout(ctypes.Structure):
@@ -61,7 +63,7 @@ EXPORTS = [
     "pqhsa_index_layout_of", "pqhsa_status_string", "pqhsa_append_workspace_bytes",
     "pqhsa_append_tokens", "pqhsa_reuse_buffer_bytes", "pqhsa_reuse_workspace_bytes",
     "pqhsa_reuse_layout_of", "pqhsa_reuse_clear", "pqhsa_reuse_decode_step",
-    "pqhsa_reuse_decode_step_profiled",
+    "pqhsa_reuse_decode_step_profiled", "pqhsa_step_flags",
 ]
 
 _lib = None
@@ -91,6 +93,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        [S, P, P, P, P, P, P, P, P, P, P, SZ, ctypes.c_int, P,
                                         ctypes.POINTER(ctypes.c_int32), P]),
         "pqhsa_workspace_layout": (ctypes.c_int, [S, ctypes.c_int, ctypes.POINTER(WsLayout)]),
+        "pqhsa_step_flags": (ctypes.c_int, [S, P, SZ, ctypes.c_int,
+                                            ctypes.POINTER(ctypes.c_uint32), P]),
         "pqhsa_append_workspace_bytes": (SZ, [S]),
         "pqhsa_append_tokens": (ctypes.c_int, [S, P, P, P, P, P, ctypes.c_int32, P, P, P, SZ, P]),
         "pqhsa_index_layout_of": (ctypes.c_int, [S, ctypes.POINTER(IndexLayout)]),
@@ -210,6 +214,17 @@ def upload_index(shape: Shape, centroids, codebooks, list_ids, codes, n_indexed,
         _ptr(index_buf, "index_buf", torch.uint8), index_buf.numel(),
         _ptr(workspace, "workspace", torch.uint8), workspace.numel(),
         _stream(stream)))
+
+
+def step_flags(shape: Shape, workspace, clear: bool = False, stream=None) -> int:
+    """The decode workspace's flags word (bit 0: a fused-step barrier wait ran
+    out); with clear=True the workspace's counters, flags and histogram are
+    zeroed afterwards.  Synchronises the stream."""
+    v = ctypes.c_uint32(0)
+    _check("pqhsa_step_flags", load().pqhsa_step_flags(
+        ctypes.byref(shape), _ptr(workspace, "workspace", torch.uint8), workspace.numel(),
+        int(bool(clear)), ctypes.byref(v), _stream(stream)))
+    return v.value
 
 
 def index_dropped(shape: Shape, index_buf, stream=None) -> int:

@@ -67,6 +67,8 @@ Dims make_dims(const pqhsa_shape* s, bool dense) {
   d.exact_only = dense ? 1 : s->exact_only;
   d.scale_log2 = (float)((double)s->scale * 1.4426950408889634);
   d.nwords = ceil_div(d.cap, 32);
+  d.fbar_extra = 0;
+  d.fbar_ticks = kBarrierTicks;
   {
     // clusters per scan block: a multiple of its 16 waves, grown until the
     // grid is about two blocks per CU, so each block's LUT copy into LDS is
@@ -245,7 +247,8 @@ pqhsa_status run_step(const pqhsa_shape* shape, const void* index_buf, const uin
                       const uint16_t* k_cache, const uint16_t* v_cache,
                       const int32_t* block_table, const int32_t* context_lens, float* out,
                       int32_t* selected, float* lse, void* workspace, size_t ws_bytes,
-                      bool staged, hipEvent_t* evs, int* n_kernels, hipStream_t stream) {
+                      bool staged, bool barrier_test, hipEvent_t* evs, int* n_kernels,
+                      hipStream_t stream) {
   PQHSA_TRY(validate(shape, false));
   if (!index_buf || !q || !k_cache || !v_cache || !block_table || !context_lens || !out ||
       !workspace)
@@ -260,10 +263,16 @@ pqhsa_status run_step(const pqhsa_shape* shape, const void* index_buf, const uin
   a.q = q; a.kc = k_cache; a.vc = v_cache; a.table = block_table; a.ctx = context_lens;
   a.out = out; a.selected = selected; a.max_sel = max_selected(shape); a.lse = lse;
   const int fP = staged ? 0 : fused_blocks_per_head(d);
+  if (barrier_test && fP == 0) return PQHSA_ERR_UNSUPPORTED;
   if (fP > 0) {
     // the whole step in one kernel
     a.d.fP = fP;
     a.d.fcpb = ceil_div(d.L, fP);
+    if (barrier_test) {
+      // one arrival more than there are blocks: every barrier wait runs out
+      a.d.fbar_extra = 1;
+      a.d.fbar_ticks = kBarrierTestTicks;
+    }
     PQHSA_TRY(hip_status(launch_fused(a, stage(evs, 0, stream))));
     if (n_kernels) *n_kernels = 1;
     return PQHSA_OK;
@@ -484,6 +493,7 @@ pqhsa_status pqhsa_append_tokens(const pqhsa_shape* shape, void* index_buf,
   aa.snap_pos = reinterpret_cast<int32_t*>(ws + lw.pos);
   aa.snap_list = reinterpret_cast<int32_t*>(ws + lw.list);
   aa.best = reinterpret_cast<unsigned long long*>(ws + lw.best);
+  aa.max_new = max_new;
   // 1. snapshot the cluster offsets and the cluster-major arrays
   PQHSA_TRY(hip_status(launch_append_snapshot(aa, stream)));
   // 2. encode the new tokens (reads the index's current n_indexed)
@@ -516,7 +526,8 @@ pqhsa_status pqhsa_decode_step(const pqhsa_shape* shape, const void* index_buf,
                                float* lse, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
   return run_step(shape, index_buf, q, k_cache, v_cache, block_table, context_lens, out,
-                  selected, lse, workspace, workspace_bytes, false, nullptr, nullptr, stream);
+                  selected, lse, workspace, workspace_bytes, false, false, nullptr, nullptr,
+                  stream);
 }
 
 pqhsa_status pqhsa_dense_decode_step(const pqhsa_shape* shape, const uint16_t* q,
@@ -542,9 +553,10 @@ pqhsa_status pqhsa_decode_step_profiled(const pqhsa_shape* shape, const void* in
   switch (variant) {
     case PQHSA_VARIANT_DEFAULT:
     case PQHSA_VARIANT_STAGED:
+    case PQHSA_VARIANT_BARRIER_TEST:
       st = run_step(shape, index_buf, q, k_cache, v_cache, block_table, context_lens, out,
                     selected, lse, workspace, workspace_bytes, variant == PQHSA_VARIANT_STAGED,
-                    events, &nk, stream);
+                    variant == PQHSA_VARIANT_BARRIER_TEST, events, &nk, stream);
       break;
     case PQHSA_VARIANT_DENSE:
       st = run_dense(shape, q, k_cache, v_cache, block_table, context_lens, out, lse, workspace,
@@ -568,6 +580,36 @@ pqhsa_status pqhsa_workspace_layout(const pqhsa_shape* shape, int dense, pqhsa_w
   out->n_exact_splits = d.n_exact_splits;
   out->n_bg_splits = d.n_bg_splits;
   out->n_parts = d.n_parts;
+  out->hist = l.hist;
+  out->hist_bytes = dense ? 0 : (size_t)d.B * d.Hkv * kHistBins * sizeof(uint32_t);
+  out->counters = l.fsync;
+  out->counters_bytes = dense ? 0 : l.fpart - l.fsync;
+  out->total = l.total;
+  return PQHSA_OK;
+}
+
+pqhsa_status pqhsa_step_flags(const pqhsa_shape* shape, void* workspace, size_t workspace_bytes,
+                              int clear, uint32_t* flags, hipStream_t stream) {
+  PQHSA_TRY(validate(shape, false));
+  if (!workspace || !flags) return PQHSA_ERR_INVALID_ARG;
+  const Dims d = make_dims(shape, false);
+  const WsLayout l = ws_layout(d, false);
+  if (workspace_bytes < l.total) return PQHSA_ERR_BUFFER_TOO_SMALL;
+  char* ws = static_cast<char*>(workspace);
+  uint32_t v = 0;
+  PQHSA_TRY(hip_status(hipMemcpyAsync(&v, ws + l.fflags, sizeof(v), hipMemcpyDeviceToHost,
+                                      stream)));
+  PQHSA_TRY(hip_status(hipStreamSynchronize(stream)));
+  *flags = v;
+  if (clear) {
+    // the step's counters, per-head flags, per-block counts and histogram:
+    // everything a step expects to find cleared
+    PQHSA_TRY(hip_status(hipMemsetAsync(ws + l.hist, 0,
+                                        (size_t)d.B * d.Hkv * kHistBins * sizeof(uint32_t),
+                                        stream)));
+    PQHSA_TRY(hip_status(hipMemsetAsync(ws + l.fsync, 0, l.fpart - l.fsync, stream)));
+    PQHSA_TRY(hip_status(hipStreamSynchronize(stream)));
+  }
   return PQHSA_OK;
 }
 

@@ -64,8 +64,8 @@ __global__ __launch_bounds__(kEncThreads) void k_append_assign(AppendArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / d.Hkv, h = bh % d.Hkv;
   const int tid = threadIdx.x;
-  const int old_n = min(max(a.ix.n_indexed[b], 0), d.cap);
-  const int new_n = min(max(a.new_n_indexed[b], 0), d.cap);
+  int old_n, new_n;
+  append_span(a, b, &old_n, &new_n);
   const int t0 = old_n + blockIdx.y * kEncTokens;
   const int nt = min(kEncTokens, new_n - t0);
   if (nt <= 0) return;
@@ -198,8 +198,8 @@ __global__ __launch_bounds__(256) void k_append_snapshot(AppendArgs a) {
     a.snap_pos[base + e] = a.ix.pos[base + e];
     a.snap_list[base + e] = a.ix.ent_list[base + e];
   }
-  const int old_n = min(max(a.ix.n_indexed[b], 0), d.cap);
-  const int new_n = min(max(a.new_n_indexed[b], 0), d.cap);
+  int old_n, new_n;
+  append_span(a, b, &old_n, &new_n);
   if (e >= old_n && e < new_n) a.best[base + e] = ~0ull;
 }
 
@@ -213,8 +213,8 @@ __global__ __launch_bounds__(256) void k_append_pq(AppendArgs a) {
   const int lane = threadIdx.x & 63;
   const int quarter = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = blockIdx.z;
-  const int old_n = min(max(a.ix.n_indexed[b], 0), d.cap);
-  const int new_n = min(max(a.new_n_indexed[b], 0), d.cap);
+  int old_n, new_n;
+  append_span(a, b, &old_n, &new_n);
   const int t0 = old_n + blockIdx.y * kEncTokens;
   const int nt = min(kEncTokens, new_n - t0);
   if (nt <= 0) return;
@@ -296,8 +296,13 @@ __global__ __launch_bounds__(256) void k_append_means(AppendArgs a) {
   const int row = lane >> 4, l16 = lane & 15;
   const int c = blockIdx.y * 4 + wave;
   // the index now covers the new tokens (nothing in this kernel reads it)
-  if (blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < d.B; i += blockDim.x) a.ix.n_indexed[i] = a.new_n_indexed[i];
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int i = threadIdx.x; i < d.B; i += blockDim.x) {
+      int o, n;
+      append_span(a, i, &o, &n);
+      a.ix.n_indexed[i] = n;
+    }
+  }
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int n_old = 0, n_new = 0;
   if (c < d.L) {
@@ -378,8 +383,8 @@ __global__ __launch_bounds__(1024) void k_append_place(AppendArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / d.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  const int old_n = min(max(a.ix.n_indexed[b], 0), d.cap);
-  const int new_n = min(max(a.new_n_indexed[b], 0), d.cap);
+  int old_n, new_n;
+  append_span(a, b, &old_n, &new_n);
   const size_t base = (size_t)bh * d.cap;
   int32_t* off = a.ix.list_off + (size_t)bh * (L + 1);
   const int32_t* oo = a.old_off + (size_t)bh * (L + 1);

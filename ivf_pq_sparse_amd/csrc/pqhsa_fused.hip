@@ -44,14 +44,16 @@
 // arrives early only waits for blocks that are already running.  (A cooperative
 // launch would guarantee the same but costs tens of µs per launch.)  If CUs
 // are withheld, waits are bounded in time: a wait that runs out sets bit 0 of
-// the workspace flags and the step goes on, so a call always finishes.
+// the workspace flags and the head's own flag, and the step goes on, so a call
+// always finishes; the head's last block then writes NaN to the head's outputs
+// instead of a result.  Counts read across blocks are clamped to each block's
+// own entry range, so that whatever a late block left behind, every access
+// stays inside its array.
 #include "pqhsa_internal.hpp"
 
 namespace pqhsa {
 
 namespace {
-
-constexpr unsigned long long kBarrierTimeout = 200000000ull;   // 2 s of the 100 MHz clock
 
 template <int G>
 struct FusedCfg {
@@ -121,7 +123,8 @@ __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0xF70); 
 // issue loads of its own data while it waits.  Arrive: every thread's memory
 // operations have completed, then one thread adds to the head's counter (true
 // in thread 0 when this block arrived last).  Wait: thread 0 polls until all
-// have arrived or the time bound has passed (then bit 0 of *flags is set).
+// have arrived or `ticks` of the 100 MHz clock have passed; then bit 0 of
+// *flags and of *hflag (the head's own word) are set.
 __device__ bool barrier_arrive(uint32_t* ctr, uint32_t n) {
   wait_mem();
   __syncthreads();
@@ -131,13 +134,15 @@ __device__ bool barrier_arrive(uint32_t* ctr, uint32_t n) {
   return last;
 }
 
-__device__ void barrier_wait(uint32_t* ctr, uint32_t n, uint32_t* flags, bool last) {
+__device__ void barrier_wait(uint32_t* ctr, uint32_t n, uint32_t* flags, uint32_t* hflag,
+                             unsigned int ticks, bool last) {
   if (threadIdx.x == 0 && !last) {
     const unsigned long long t0 = wall_clock64();
     while (ld_dev(ctr) < n) {
       __builtin_amdgcn_s_sleep(8);
-      if (wall_clock64() - t0 > kBarrierTimeout) {
+      if (wall_clock64() - t0 > ticks) {
         __hip_atomic_fetch_or(flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(hflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
@@ -323,6 +328,9 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   // the head's three counters (barrier 1, barrier 2, finished blocks), each on
   // its own cache line: heads and counters do not contend for one line
   uint32_t* sync = a.ws.fsync + (size_t)bh * 3 * kSyncStride;
+  // the head's timeout flag shares the finished-blocks line
+  uint32_t* hflag = sync + 2 * kSyncStride + 1;
+  const uint32_t nbar = (uint32_t)(P + d.fbar_extra);   // arrivals a barrier waits for
   uint32_t* ghist = a.ws.hist + (size_t)bh * kHistBins;
   // the top 16 bits of each entry's selection key (0: not a candidate),
   // enough for the 12-bit buckets; a tie's full key is recomputed from its
@@ -572,7 +580,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       if (v) __hip_atomic_fetch_add(&ghist[i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  const bool last1 = barrier_arrive(&sync[0], (uint32_t)P);
+  const bool last1 = barrier_arrive(&sync[0], nbar);
   // while waiting: this block's first keys for the classification below
   constexpr int kPer = 16;
   uint32_t pk[kPer];
@@ -581,7 +589,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     const int e = E0 + u * NT + tid;
     pk[u] = e < E1 ? keys[e] : 0u;
   }
-  barrier_wait(&sync[0], (uint32_t)P, a.ws.fflags, last1);
+  barrier_wait(&sync[0], nbar, a.ws.fflags, hflag, d.fbar_ticks, last1);
 
   // ======================================================= phase 2: threshold bucket
   // the head's histogram from read_lo up: exact there, because every block
@@ -724,7 +732,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   if (tid == 0)
     st_dev(&a.ws.fcnt[(size_t)bh * kMaxFusedP + sub],
            ((unsigned long long)(uint32_t)nt << 32) | (uint32_t)na);
-  const bool last2 = barrier_arrive(&sync[kSyncStride], (uint32_t)P);
+  const bool last2 = barrier_arrive(&sync[kSyncStride], nbar);
   // while waiting: this block's own tie records' clusters and weights into LDS
   // (the histogram region is free until the background logits), so that
   // placing its winners needs no global load
@@ -740,7 +748,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) ownw[i * G + g] = ow[g];
   }
-  barrier_wait(&sync[kSyncStride], (uint32_t)P, a.ws.fflags, last2);
+  barrier_wait(&sync[kSyncStride], nbar, a.ws.fflags, hflag, d.fbar_ticks, last2);
 
   // ======================================================= phase 3: ties, rows, partials
   // the queries for the exact rows (packed bf16, 8 dims per lane of a 16-lane
@@ -750,13 +758,21 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   for (int g = 0; g < G; ++g) qp[g] = *reinterpret_cast<const uint4*>(qh + g * kD + (tid & 15) * 8);
   if (tid < 64) {
     unsigned long long v = 0;
-    if (tid < P) v = ld_dev(&a.ws.fcnt[(size_t)bh * kMaxFusedP + tid]);
-    const int ca = (int)(uint32_t)v, ct = (int)(v >> 32);
+    int jb = 0, je = 0;   // block tid's entries [jb, je)
+    if (tid < P) {
+      v = ld_dev(&a.ws.fcnt[(size_t)bh * kMaxFusedP + tid]);
+      jb = entry_at(min(tid * d.fcpb, d.L));
+      je = max(jb, entry_at(min((tid + 1) * d.fcpb, d.L)));
+    }
+    // a block lists at most its own entries; clamping keeps every record
+    // index inside the block's range even after a barrier wait ran out
+    const int ca = min((int)min((uint32_t)v, 0x7fffffffu), je - jb);
+    const int ct = min((int)min((uint32_t)(v >> 32), 0x7fffffffu), je - jb - ca);
     const int xa = wave_incl_scan(ca), xt = wave_incl_scan(ct);
     if (tid < P) {
       S.apre[tid] = xa - ca;
       S.tpre[tid] = xt - ct;
-      S.tbase[tid] = entry_at(min(tid * d.fcpb, d.L));
+      S.tbase[tid] = jb;
     }
     if (tid == 63) { S.apre[P] = xa; S.tpre[P] = xt; }
   }
@@ -1052,7 +1068,10 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   // ======================================================= last block of the head
   // every (head, dim) thread loads its column of the P partials (a wave's
   // loads of one partial are contiguous) while one wave per head loads the
-  // (m, l) pairs and forms the weights of the partials against the head's max
+  // (m, l) pairs and forms the weights of the partials against the head's max.
+  // A head one of whose barrier waits ran out gets NaN instead: its partials
+  // may be built on an incomplete histogram or incomplete records.
+  const bool timed_out = ld_dev(hflag) != 0u;
   {
     float* fp = reinterpret_cast<float*>(hist);     // [G][64] weights
     float* mlh = fp + G * kMaxFusedP;               // [G][2] head max and sum
@@ -1091,9 +1110,11 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
         for (int j = 0; j < kMaxFusedP; ++j) A = fmaf(fg[j], x[j], A);
         const float M = mlh[g * 2], L = mlh[g * 2 + 1];
         const size_t bq = (size_t)b * d.Hq + h * G + g;
-        a.out[bq * kD + dim] = L > 0.0f ? A / L : 0.0f;
-        if (dim == 0 && a.lse)
-          a.lse[bq] = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+        float o = L > 0.0f ? A / L : 0.0f;
+        float ls = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+        if (timed_out) o = ls = __builtin_nanf("");
+        a.out[bq * kD + dim] = o;
+        if (dim == 0 && a.lse) a.lse[bq] = ls;
       }
     }
   }
@@ -1143,6 +1164,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     st_dev(&sync[0], 0u);
     st_dev(&sync[kSyncStride], 0u);
     st_dev(&sync[2 * kSyncStride], 0u);
+    st_dev(hflag, 0u);
   }
 }
 

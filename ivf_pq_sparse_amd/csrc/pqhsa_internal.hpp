@@ -61,7 +61,13 @@ struct Dims {
   int upload_chunks;          // counting-sort chunks per (b, h)
   int fP;                     // fused step: blocks per (b, h) (0: the staged kernels run)
   int fcpb;                   // fused step: clusters per block
+  int fbar_extra;             // fused step: arrivals a barrier waits for beyond its P blocks
+                              //   (0; 1 only in the barrier test, so that every wait runs out)
+  unsigned int fbar_ticks;    // fused step: bound of a barrier wait in ticks of the 100 MHz clock
 };
+
+constexpr unsigned int kBarrierTicks = 200000000u;   // 2 s: the fused step's default wait bound
+constexpr unsigned int kBarrierTestTicks = 2000u;    // 20 us: the barrier test's wait bound
 
 struct IndexPtrs {
   float* centroids;    // [BH][L][128]
@@ -161,7 +167,18 @@ struct AppendArgs {
   // nearest centroid found so far; the minimum over centroid splits
   unsigned long long* best;
   int asg_chunks;                // 64-centroid chunks per assignment block
+  int max_new;                   // at most this many new tokens per sequence are added
 };
+
+// Tokens [*old_n, *new_n) of sequence b that an append adds: the requested
+// span, clamped to the capacity and to max_new tokens (the rest stay in the
+// exact tail).
+__device__ __forceinline__ void append_span(const AppendArgs& a, int b, int* old_n, int* new_n) {
+  const int o = min(max(a.ix.n_indexed[b], 0), a.d.cap);
+  const int n = min(max(a.new_n_indexed[b], 0), a.d.cap);
+  *old_n = o;
+  *new_n = min(n, o + a.max_new);
+}
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

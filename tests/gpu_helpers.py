@@ -26,15 +26,31 @@ def log(msg):
     print(msg, flush=True)
 
 
+def poison_workspace(dec):
+    """Fill the decode workspace with 0xFF bytes (NaN as floats, -1 as
+    integers) except the regions a step expects cleared (histogram and the
+    fused step's counters), so that a read of anything the step did not write
+    first shows up in the outputs."""
+    lay = pq.workspace_layout(dec.shape)
+    ws = dec.workspace
+    ws.fill_(0xFF)
+    ws[lay.hist:lay.hist + lay.hist_bytes].zero_()
+    ws[lay.counters:lay.counters + lay.counters_bytes].zero_()
+    torch.cuda.synchronize()
+
+
 def run_gpu(inp, dense=False, want_selected=True, page_seed=0, spare_pages=0, max_context=None,
-            staged=False, background=True):
+            staged=False, background=True, poison=False):
     """Stage `inp`, upload the index and run one step; return numpy results.
     staged=True runs the six staged kernels instead of the default path;
-    background=False sets exact_only (no background term)."""
+    background=False sets exact_only (no background term); poison=True fills
+    the workspace's scratch with NaN bytes first."""
     tens, kw = stage(inp, "cuda", page_seed=page_seed, spare_pages=spare_pages,
                      max_context=max_context)
     shape = pq.make_shape(**kw, exact_only=0 if background else 1)
     dec = pq.PQHSADecoder(shape)
+    if poison:
+        poison_workspace(dec)
     if dense:
         out, lse = dec.dense(tens["q"], tens["k_cache"], tens["v_cache"], tens["block_table"],
                              tens["context_lens"], lse=True)
@@ -117,15 +133,22 @@ def oracle_with_details(inp, heads=None, background=True):
 
 
 def parity(inp, heads=None, what="", max_context=None, page_seed=0, staged=False,
-           background=True):
+           background=True, poison=False):
     """Full check of one step: selection within band, outputs against the
     oracle recomputed with the GPU's set, and the log-sum-exp."""
-    import oracle
     log(f"[parity] {what}: B={inp.batch} Hq={inp.num_q_heads} Hkv={inp.num_kv_heads} "
         f"T={inp.context_lens.tolist()} L={inp.num_lists} bp={inp.budget_bp} "
-        f"{'staged' if staged else 'default'}{'' if background else ' exact-only'}")
+        f"{'staged' if staged else 'default'}{'' if background else ' exact-only'}"
+        f"{' poisoned workspace' if poison else ''}")
     g = run_gpu(inp, max_context=max_context, page_seed=page_seed, staged=staged,
-                background=background)
+                background=background, poison=poison)
+    return check_result(g, inp, heads=heads, what=what, background=background)
+
+
+def check_result(g, inp, heads=None, what="", background=True):
+    """Check a GPU step result (as run_gpu returns it) against the oracle on
+    `heads` (all (sequence, KV head) pairs if None)."""
+    import oracle
     ref = oracle_with_details(inp, heads=heads, background=background)
     nd = check_selection(g["selected"], ref, heads=heads)
     sel = {k: g["selected"][k] for k in ref["selected"]}
@@ -140,7 +163,7 @@ def parity(inp, heads=None, what="", max_context=None, page_seed=0, staged=False
     gl, rl = g["lse"][bi, qi], lse_ref[bi, qi]
     # an empty sequence has lse = -inf on both sides
     both_empty = np.isneginf(gl) & np.isneginf(rl)
-    lse_err = np.where(both_empty, 0.0, np.abs(gl - rl)).max()
+    lse_err = np.abs(np.where(both_empty, 0.0, gl) - np.where(both_empty, 0.0, rl)).max()
     assert lse_err <= LSE_ATOL, f"{what}: lse error {lse_err:.3e}"
     log(f"[parity] {what}: ok max-abs={mx:.2e} l1={l1:.2e} lse={lse_err:.2e} near-tie diffs={nd}")
     return g, ref, again

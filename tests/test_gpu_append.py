@@ -4,7 +4,8 @@ oracle, and of a decode step on the appended index against the decode oracle.
 Encoder decisions are taken in fp32 on the GPU and in float64 by the oracle;
 a choice counts as correct when its distance is within the fp32 rounding
 band of the exact minimum (several choices are then correct), otherwise it
-must equal the oracle's.
+must equal the oracle's.  Where every distance is exact in fp32 (dyadic
+inputs), ties are exact too and the lower id must win on both sides.
 """
 import numpy as np
 import pytest
@@ -172,3 +173,95 @@ def test_append_into_an_empty_index():
     mu = dec.index[lay.means:lay.means + 16 * 512].view(torch.float32).cpu().numpy()
     batch = orc.cluster_means(orc.bf16_to_f64(inp.v_bits[0, 0, :2500]), gl, 16)
     np.testing.assert_allclose(mu.reshape(16, 128), batch, atol=3e-6)
+
+
+def test_append_exact_ties_take_lower_ids():
+    # Dyadic centroids and codewords with noise-free keys make every fp32
+    # distance exact; a centroid copied over a higher-numbered one and a
+    # codeword copied over a higher-numbered one make exact ties.  The
+    # encoder must take the lower list and the lower codeword every time, and
+    # so equal the oracle token for token.
+    from oracle import pqhsa_append as ap
+    L, tail, T = 16, 600, 3000
+    inp = make_step_inputs(1, context_lens=[T], num_q_heads=4, num_kv_heads=1, num_lists=L,
+                           n_tail=tail, dyadic=True, noise=0.0, workload_id=322)
+    old = int(inp.n_indexed[0])
+    lists_tail = inp.list_ids[0, 0, old:T]
+    a = int(np.bincount(lists_tail, minlength=L).argmax())     # a list with many new tokens
+    b = L - 1 if a != L - 1 else L - 2
+    assert a < b
+    inp.centroids[0, 0, b] = inp.centroids[0, 0, a]
+    m = 5
+    codes_m = inp.codes[0, 0, old:T, m][lists_tail == a]
+    j1 = int(np.bincount(codes_m, minlength=256).argmax())
+    j2 = 255 if j1 != 255 else 254
+    assert j1 < j2
+    inp.codebooks[0, 0, m, j2] = inp.codebooks[0, 0, m, j1]
+    tens, shape, dec = _setup(inp)
+    tens["list_ids"][0, :, old:] = -7
+    tens["codes"][0, :, old:] = 0
+    new_n = torch.tensor([T], dtype=torch.int32, device="cuda")
+    log(f"[append] planted ties: lists {a}/{b}, subspace {m} codewords {j1}/{j2}")
+    dec.append(tens["k_cache"], tens["v_cache"], tens["block_table"], new_n, tail,
+               tens["list_ids"], tens["codes"])
+    torch.cuda.synchronize()
+    gl = tens["list_ids"].cpu().numpy()[0, 0, old:T]
+    gc = tens["codes"].cpu().numpy()[0, 0, old:T].astype(np.int64)
+    K = _f64(inp.k_bits[0, 0, old:T])
+    ol, oc = ap.encode_tokens(K, inp.centroids[0, 0].astype(np.float64),
+                              inp.codebooks[0, 0].astype(np.float64))
+    n_tied_l = int((lists_tail == a).sum())
+    n_tied_c = int(((lists_tail == a) & (inp.codes[0, 0, old:T, m] == j1)).sum())
+    assert n_tied_l > 0 and n_tied_c > 0
+    assert not np.any(gl == b), "an exact list tie went to the higher list"
+    assert not np.any(gc[:, m] == j2), "an exact codeword tie went to the higher codeword"
+    assert np.array_equal(gl, ol) and np.array_equal(gc, oc)
+    log(f"[append] {n_tied_l} list ties and {n_tied_c} codeword ties, all to the lower id")
+
+
+def test_append_more_tokens_than_max_new():
+    # max_new bounds every sequence's append: only that many tokens join the
+    # index, the rest stay in the exact tail (unencoded), and a decode step on
+    # the result matches the oracle with that shorter index
+    import ivf_pq_sparse_amd as pq
+    import oracle
+    from gpu_helpers import oracle_with_details
+    inp = make_step_inputs(1, context_lens=[4000, 3500], batch=2, num_q_heads=8, num_kv_heads=2,
+                           num_lists=32, n_tail=300, budget_bp=150, workload_id=323)
+    tens, shape, dec = _setup(inp)
+    old = inp.n_indexed.copy()
+    for b in range(2):
+        tens["list_ids"][b, :, old[b]:] = -7
+    max_new = 100
+    new_n = torch.tensor(inp.context_lens, dtype=torch.int32, device="cuda")
+    log("[append] 300 new tokens per sequence requested, max_new 100")
+    dec.append(tens["k_cache"], tens["v_cache"], tens["block_table"], new_n, max_new,
+               tens["list_ids"], tens["codes"])
+    torch.cuda.synchronize()
+    lay = pq.index_layout(shape)
+    n_idx = dec.index[lay.n_indexed:lay.n_indexed + 8].view(torch.int32).cpu().numpy()
+    assert list(n_idx) == [int(o) + max_new for o in old]
+    gl = tens["list_ids"].cpu().numpy()
+    gc = tens["codes"].cpu().numpy()
+    for b in range(2):
+        assert np.all(gl[b, :, old[b]:old[b] + max_new] >= 0)
+        assert np.all(gl[b, :, old[b] + max_new:inp.context_lens[b]] == -7)
+    L = shape.num_lists
+    off = dec.index[lay.list_off:lay.list_off + 2 * 2 * (L + 1) * 4].view(torch.int32)
+    off = off.cpu().numpy().reshape(2, 2, L + 1)
+    assert np.all(off[:, :, L] == (old + max_new)[:, None])
+    inp.n_indexed = (old + max_new).astype(np.int32)
+    for b in range(2):
+        n = int(inp.n_indexed[b])
+        inp.list_ids[b, :, :n] = gl[b, :, :n]
+        inp.codes[b, :, :n] = gc[b, :, :n]
+    out, sel, lse = dec.step(tens["q"], tens["k_cache"], tens["v_cache"], tens["block_table"],
+                             tens["context_lens"], selected=True, lse=True)
+    torch.cuda.synchronize()
+    assert dec.flags() == 0
+    ref = oracle_with_details(inp)
+    s = sel.cpu().numpy()
+    gsel = {(b, h): s[b, h][s[b, h] >= 0].astype(np.int64) for b in range(2) for h in range(2)}
+    check_selection(gsel, ref)
+    again = oracle.decode_step(inp, selected=gsel)
+    check_output(out.cpu().numpy().astype(np.float64), again["O"], "decode after a capped append")

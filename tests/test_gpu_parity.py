@@ -15,8 +15,8 @@ def _need_gpu():
     pq.load()          # raises if the HIP library is not built: no fallback
 
 
-from gpu_helpers import (check_output, log, oracle_with_details, parity,  # noqa: E402
-                         run_gpu)
+from gpu_helpers import (check_output, check_result, log, oracle_with_details,  # noqa: E402
+                         parity, run_gpu)
 from pqhsa_synth import make_step_inputs  # noqa: E402
 
 
@@ -52,16 +52,28 @@ def test_llama_32k_parity():
 
 
 # Full-size workloads in the launch configuration bench.py times (same shape
-# fields, so the same grids): every head at 128K and 512K, sampled heads of
-# the 16-sequence batch, each head checked against the oracle in full.
+# fields, so the same grids): every head at 128K, at 512K and of the
+# 16-sequence batch, each head checked against the oracle in full.
 def test_llama_128k_parity():
     parity(make_step_inputs(2), what="workload 2 (128K, 32q/8kv, L512, k=1311)")
 
 
-def test_llama_128k_batch16_parity_sampled_heads():
-    heads = [(0, 0), (3, 5), (7, 2), (10, 7), (15, 1), (15, 6)]
-    parity(make_step_inputs(3), heads=heads,
-           what="workload 3 (16 x 128K, 32q/8kv, L512), 6 sampled (seq, KV head)")
+@pytest.fixture(scope="module")
+def batch16_run():
+    """One GPU step of the 16-sequence batch (two fused blocks per head, the
+    scan's cluster-claim path), shared by the four checks below."""
+    inp = make_step_inputs(3)
+    log("[parity] workload 3 (16 x 128K, 32q/8kv, L512): one GPU step")
+    return inp, run_gpu(inp)
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_llama_128k_batch16_parity(batch16_run, part):
+    # every (sequence, KV head) of the batch, four sequences per test
+    inp, g = batch16_run
+    heads = [(b, h) for b in range(4 * part, 4 * part + 4) for h in range(inp.num_kv_heads)]
+    check_result(g, inp, heads=heads,
+                 what=f"workload 3 (16 x 128K), sequences {4 * part}..{4 * part + 3}, all KV heads")
 
 
 def test_qwen_512k_parity():
@@ -414,3 +426,52 @@ def test_largest_list_count():
     inp = make_step_inputs(1, context_lens=[40000], num_q_heads=8, num_kv_heads=2,
                            num_lists=16384, budget_bp=200, workload_id=52)
     parity(inp, what="16384 lists over 40K tokens")
+
+
+@pytest.mark.parametrize("staged", [False, True])
+def test_poisoned_workspace_parity(staged):
+    # every scratch byte NaN (0xFF) before the step, counters and histogram
+    # aside: a read of a partial, record or key the step did not write first
+    # would reach the outputs
+    parity(make_step_inputs(1), what="workload 1", staged=staged, poison=True)
+    inp = make_step_inputs(1, context_lens=[5000, 3333, 777], batch=3, num_q_heads=16,
+                           num_kv_heads=2, num_lists=64, n_tail=40, budget_bp=250,
+                           workload_id=61)
+    parity(inp, what="ragged batch", staged=staged, poison=True, page_seed=6)
+
+
+def test_barrier_timeout_is_reported_and_cleared():
+    # The barrier test variant waits for one block more than the grid has and
+    # gives up after 20 us, so every wait runs out while every kernel still
+    # ends normally: the call returns, the flag is set and every output is
+    # NaN.  After the flag is read and the workspace cleared, the next step
+    # matches the oracle.
+    import ivf_pq_sparse_amd as pq
+    from pqhsa_synth.device import stage
+    inp = make_step_inputs(1)
+    tens, kw = stage(inp, "cuda")
+    shape = pq.make_shape(**kw)
+    dec = pq.PQHSADecoder(shape)
+    dec.upload(tens["centroids"], tens["codebooks"], tens["list_ids"], tens["codes"],
+               tens["n_indexed"], tens["v_cache"], tens["block_table"])
+    out = torch.zeros(shape.batch, shape.num_q_heads, 128, device="cuda")
+    lse = torch.zeros(shape.batch, shape.num_q_heads, device="cuda")
+    evs = [pq.HipEvent() for _ in range(2 * pq.NUM_STAGES)]
+    log("[barrier] fused step with one phantom arrival per barrier")
+    n = pq.decode_step_profiled(shape, dec.index, tens["q"], tens["k_cache"], tens["v_cache"],
+                                tens["block_table"], tens["context_lens"], out, dec.workspace,
+                                evs, variant=pq.VARIANT_BARRIER_TEST, lse=lse)
+    torch.cuda.synchronize()
+    assert n == 1
+    assert torch.isnan(out).all() and torch.isnan(lse).all()
+    assert dec.flags(clear=True) & 1
+    assert dec.flags() == 0
+    out2, sel, lse2 = dec.step(tens["q"], tens["k_cache"], tens["v_cache"], tens["block_table"],
+                               tens["context_lens"], selected=True, lse=True)
+    torch.cuda.synchronize()
+    assert dec.flags() == 0
+    s = sel.cpu().numpy()
+    g = dict(O=out2.cpu().numpy().astype(np.float64), lse=lse2.cpu().numpy(),
+             selected={(b, h): s[b, h][s[b, h] >= 0].astype(np.int64)
+                       for b in range(shape.batch) for h in range(shape.num_kv_heads)})
+    check_result(g, inp, what="step after a cleared barrier timeout")
