@@ -223,6 +223,31 @@ pqhsa_status pqhsa_decode_step(const pqhsa_shape* shape, const void* index_buf,
                                hipStream_t stream);
 
 /*
+ * pqhsa_decode_step without a workspace argument, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments (minus workspace), same results and
+ * same kernels as pqhsa_decode_step, plus one small kernel that clears the
+ * step's counters first.  Scratch comes from a fixed array of
+ * PQHSA_NOALLOC_SCRATCH_BYTES in the library, one per device, held until the
+ * process ends; nothing is allocated or freed.  Shapes whose workspace
+ * (pqhsa_workspace_bytes(shape, 0)) exceeds it return
+ * PQHSA_ERR_BUFFER_TOO_SMALL and enqueue nothing (128 MiB covers, e.g., one
+ * sequence of 131072 tokens with 8 KV heads; not 16 such sequences).
+ * Every call on a device shares that device's array: calls that overlap on
+ * one device (other streams, other threads) race and must be ordered by the
+ * caller.  A barrier wait that runs out leaves NaN outputs as in
+ * pqhsa_decode_step; the next call starts from cleared counters.  Errors: as
+ * pqhsa_decode_step; PQHSA_ERR_HIP also if the array's address cannot be
+ * found.
+ */
+#define PQHSA_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+pqhsa_status pqhsa_decode_step_noalloc(const pqhsa_shape* shape, const void* index_buf,
+                                       const uint16_t* q, const uint16_t* k_cache,
+                                       const uint16_t* v_cache, const int32_t* block_table,
+                                       const int32_t* context_lens, float* out,
+                                       int32_t* selected, float* lse, hipStream_t stream);
+
+/*
  * Dense split-K decode attention over each sequence's whole context, through
  * the same exact-attention and merge kernels as pqhsa_decode_step.  This is
  * the honest baseline: the activation/KV-sparsity crossover article

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     append_tokens,
     append_workspace_bytes,
+    NOALLOC_SCRATCH_BYTES,
     NUM_STAGES,
     VARIANT_BARRIER_TEST,
     VARIANT_DEFAULT,
@@ -26,6 +27,7 @@ from ._lib import (  # noqa: F401
     ReuseLayout,
     Shape,
     decode_step,
+    decode_step_noalloc,
     decode_step_profiled,
     dense_decode_step,
     index_bytes,

@@ -63,8 +63,9 @@ EXPORTS = [
     "pqhsa_index_layout_of", "pqhsa_status_string", "pqhsa_append_workspace_bytes",
     "pqhsa_append_tokens", "pqhsa_reuse_buffer_bytes", "pqhsa_reuse_workspace_bytes",
     "pqhsa_reuse_layout_of", "pqhsa_reuse_clear", "pqhsa_reuse_decode_step",
-    "pqhsa_reuse_decode_step_profiled", "pqhsa_step_flags",
+    "pqhsa_reuse_decode_step_profiled", "pqhsa_step_flags", "pqhsa_decode_step_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 
 _lib = None
 
@@ -89,6 +90,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "pqhsa_index_dropped": (ctypes.c_int, [S, P, ctypes.POINTER(ctypes.c_int64), P]),
         "pqhsa_decode_step": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "pqhsa_dense_decode_step": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, SZ, P]),
+        "pqhsa_decode_step_noalloc": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, P, P]),
         "pqhsa_decode_step_profiled": (ctypes.c_int,
                                        [S, P, P, P, P, P, P, P, P, P, P, SZ, ctypes.c_int, P,
                                         ctypes.POINTER(ctypes.c_int32), P]),
@@ -256,6 +258,19 @@ def decode_step(shape: Shape, index_buf, q, k_cache, v_cache, block_table, conte
     _check("pqhsa_decode_step", load().pqhsa_decode_step(
         ctypes.byref(shape), _ptr(index_buf, "index_buf", torch.uint8), qp, kp, vp, tp, cp, op,
         sp, lp, _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+
+
+def decode_step_noalloc(shape: Shape, index_buf, q, k_cache, v_cache, block_table,
+                        context_lens, out, selected=None, lse=None, stream=None):
+    """pqhsa_decode_step_noalloc: the decode step on the library's fixed
+    per-device scratch (no workspace argument)."""
+    qp, kp, vp, tp, cp, op, lp = _step_ptrs(shape, q, k_cache, v_cache, block_table,
+                                            context_lens, out, lse)
+    sp = _ptr(selected, "selected", torch.int32,
+              shape.batch * shape.num_kv_heads * max(max_selected(shape), 1), optional=True)
+    _check("pqhsa_decode_step_noalloc", load().pqhsa_decode_step_noalloc(
+        ctypes.byref(shape), _ptr(index_buf, "index_buf", torch.uint8), qp, kp, vp, tp, cp, op,
+        sp, lp, _stream(stream)))
 
 
 def dense_decode_step(shape: Shape, q, k_cache, v_cache, block_table, context_lens, out,

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "pqhsa_internal.hpp"
 
@@ -399,6 +400,48 @@ pqhsa_status run_reuse(const pqhsa_shape* shape, int32_t window, float max_dist2
   return PQHSA_OK;
 }
 
+// ---------------------------------------------------------------- fixed scratch
+// The workspace of pqhsa_decode_step_noalloc: one array per device, held
+// until the process ends.  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)PQHSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+void* g_scratch[kScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch (looked up on the first
+// call on that device), or nullptr with *err set.
+void* scratch_ptr(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kScratchDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
+// Zero two byte ranges (16-byte aligned, multiples of 16 bytes) with plain
+// vector stores: a kernel rather than a memset, so that the clearing can sit
+// in a captured graph.
+__global__ __launch_bounds__(256) void k_zero2(uint4* a, size_t na, uint4* b, size_t nb) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < na + nb; i += stride) {
+    if (i < na) a[i] = make_uint4(0, 0, 0, 0);
+    else b[i - na] = make_uint4(0, 0, 0, 0);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -528,6 +571,34 @@ pqhsa_status pqhsa_decode_step(const pqhsa_shape* shape, const void* index_buf,
   return run_step(shape, index_buf, q, k_cache, v_cache, block_table, context_lens, out,
                   selected, lse, workspace, workspace_bytes, false, false, nullptr, nullptr,
                   stream);
+}
+
+pqhsa_status pqhsa_decode_step_noalloc(const pqhsa_shape* shape, const void* index_buf,
+                                       const uint16_t* q, const uint16_t* k_cache,
+                                       const uint16_t* v_cache, const int32_t* block_table,
+                                       const int32_t* context_lens, float* out,
+                                       int32_t* selected, float* lse, hipStream_t stream) {
+  PQHSA_TRY(validate(shape, false));
+  const Dims d = make_dims(shape, false);
+  const WsLayout l = ws_layout(d, false);
+  if (!index_buf || !q || !k_cache || !v_cache || !block_table || !context_lens || !out)
+    return PQHSA_ERR_INVALID_ARG;
+  if (l.total > kScratchBytes) return PQHSA_ERR_BUFFER_TOO_SMALL;
+  hipError_t e = hipSuccess;
+  char* ws = static_cast<char*>(scratch_ptr(&e));
+  if (!ws) return PQHSA_ERR_HIP;
+  // the histogram, counters and flags start at zero: the previous call on
+  // this device may have used another shape (another layout of the array)
+  const size_t hist_bytes = (size_t)d.B * d.Hkv * kHistBins * sizeof(uint32_t);
+  const size_t ctr_bytes = l.fpart - l.fsync;
+  const size_t n16 = (hist_bytes + ctr_bytes) / 16;
+  const int blocks = (int)std::min<size_t>(1024, (n16 + 255) / 256);
+  hipLaunchKernelGGL(k_zero2, dim3(blocks), dim3(256), 0, stream,
+                     reinterpret_cast<uint4*>(ws + l.hist), hist_bytes / 16,
+                     reinterpret_cast<uint4*>(ws + l.fsync), ctr_bytes / 16);
+  PQHSA_TRY(hip_status(hipGetLastError()));
+  return run_step(shape, index_buf, q, k_cache, v_cache, block_table, context_lens, out,
+                  selected, lse, ws, kScratchBytes, false, false, nullptr, nullptr, stream);
 }
 
 pqhsa_status pqhsa_dense_decode_step(const pqhsa_shape* shape, const uint16_t* q,

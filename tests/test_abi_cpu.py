@@ -151,6 +151,33 @@ def test_null_pointers_and_small_buffers(lib, shape):
     assert lib.pqhsa_index_layout_of(None, None) == INVALID
 
 
+def test_noalloc_and_flags_validation(lib, shape):
+    # the fixed-scratch step refuses a shape whose workspace exceeds the
+    # scratch, and bad arguments, before it touches the device
+    import ivf_pq_sparse_amd as pq
+    fake = ctypes.c_void_p(0x1000)
+    S = ctypes.byref(shape)
+    assert pq.workspace_bytes(shape) <= pq.NOALLOC_SCRATCH_BYTES
+    for i in range(7):
+        args = [fake] * 7
+        args[i] = None
+        assert lib.pqhsa_decode_step_noalloc(S, *args, None, None, None) == INVALID
+    big = pq.make_shape(batch=16, num_q_heads=32, num_kv_heads=8, num_pages=16 * 8192,
+                        max_pages_per_seq=8192, max_context=131072, num_lists=512, n_sink=4,
+                        n_recent=128, budget_bp=100)
+    assert pq.workspace_bytes(big) > pq.NOALLOC_SCRATCH_BYTES
+    assert lib.pqhsa_decode_step_noalloc(ctypes.byref(big), *([fake] * 7), None, None,
+                                         None) == TOO_SMALL
+    shape.budget_bp = -5
+    assert lib.pqhsa_decode_step_noalloc(S, *([fake] * 7), None, None, None) == INVALID
+    shape.budget_bp = 100
+    flags = ctypes.c_uint32(0)
+    need = lib.pqhsa_workspace_bytes(S, 0)
+    assert lib.pqhsa_step_flags(S, None, need, 0, ctypes.byref(flags), None) == INVALID
+    assert lib.pqhsa_step_flags(S, fake, need, 0, None, None) == INVALID
+    assert lib.pqhsa_step_flags(S, fake, need - 1, 1, ctypes.byref(flags), None) == TOO_SMALL
+
+
 def test_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     import ivf_pq_sparse_amd as pq
