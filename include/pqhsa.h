@@ -318,8 +318,11 @@ pqhsa_status pqhsa_decode_step_profiled(const pqhsa_shape* shape, const void* in
  *           out (its results are then not valid)
  * The staged step fills lut, qc, keys, bins, rows, n_rows and partials; the
  * fused step fills qc and bins of every cluster, n_rows, rows in a per-block
- * order, and at the start of keys the top 16 bits of each key as
- * uint16 [B*Hkv][max_context]. */
+ * order, and at the start
+ * of keys a 16-bit code of each key as uint16 [B*Hkv][max_context]: the
+ * order key's sign, its binary exponent clamped to the 16 binades of
+ * [2^-7, 2^9) (the same field range in both halves), then 11 mantissa bits,
+ * at least 1 (0 for non-candidates). */
 /* Also: hist (uint32 [B*Hkv][4096] key histogram, hist_bytes long) and
  * counters (the fused step's per-head barrier counters and flags, the flags
  * word and per-block counts, counters_bytes long): the regions a step expects

@@ -76,7 +76,10 @@ struct FusedCfg {
   static_assert((size_t)kItems * sizeof(long long) + 4096 <= kHBytes, "item staging");
 };
 
+constexpr int kRankMax = 512;   // threshold-bucket ties resolved by counting ranks
+
 struct FusedStatic {
+  unsigned long long thr;   // the r-th largest tie composite
   int nextc;        // the scan's next unclaimed cluster of the block
   int sh[40];
   uint32_t rh[256];
@@ -157,7 +160,7 @@ __device__ void block_scan2(int a, int b, int* oa, int* ob, int* ta, int* tb, in
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int xa = wave_incl_scan(a), xb = wave_incl_scan(b);
   if (lane == 63) { sh[wave] = xa; sh[NW + 1 + wave] = xb; }
-  __syncthreads();
+  lds_sync();
   if (threadIdx.x == 0) {
     int ra = 0, rb = 0;
     for (int w = 0; w < NW; ++w) {
@@ -168,12 +171,12 @@ __device__ void block_scan2(int a, int b, int* oa, int* ob, int* ta, int* tb, in
     sh[NW] = ra;
     sh[2 * NW + 1] = rb;
   }
-  __syncthreads();
+  lds_sync();
   *oa = sh[wave] + xa - a;
   *ob = sh[NW + 1 + wave] + xb - b;
   *ta = sh[NW];
   *tb = sh[2 * NW + 1];
-  __syncthreads();
+  lds_sync();
 }
 
 // The whole block, over bins [lo, 4096) of a histogram in LDS (bin = top 12
@@ -203,7 +206,7 @@ __device__ void block_threshold(const uint32_t* hist, int lo, int k, int* out, i
   for (int i = 0; i < PER; ++i) s += (hi - PER + i >= lo) ? (int)v[i] : 0;
   const int inc = wave_incl_scan(s);
   if (lane == 63) sh[wave] = inc;
-  __syncthreads();
+  lds_sync();
   int before = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -224,12 +227,34 @@ __device__ void block_threshold(const uint32_t* hist, int lo, int k, int* out, i
     out[0] = beta; out[1] = run; out[2] = tot;
   }
   if (kk == 0 && tid == 0) { out[0] = -1; out[1] = 0; out[2] = tot; }
-  __syncthreads();
+  lds_sync();
 }
 
+// 16-bit code of an order key, monotone (a larger key never gets a smaller
+// code): the sign, the binary exponent clamped to a window of 16 binades
+// (|x| in [2^-7, 2^9), where base-2 logits of interest lie), then 11 mantissa
+// bits.  Its top 12 bits are the histogram bin: 128 bins per binade, 16 times
+// finer than the key's own top 12 bits, so that far fewer keys share the
+// threshold bin.  Keys outside the window share the window's edge bins, and
+// ties are resolved on the full key, so selection stays exact for any input.
+// 0 stays reserved for "not a candidate".
+constexpr int kWinLo = 127 - 7;   // lowest biased exponent of the window
+__device__ __forceinline__ uint32_t key_code16(uint32_t u) {
+  const uint32_t s = u >> 31;
+  // the exponent field of the order key: e for x >= 0, 255 - e below 0; the
+  // window is the same field range [kWinLo, kWinLo + 15] in both halves
+  const int f = (int)((u >> 23) & 0xffu);
+  uint32_t v;
+  if (f < kWinLo) v = 0;
+  else if (f > kWinLo + 15) v = 0x7fffu;
+  else v = ((uint32_t)(f - kWinLo) << 11) | ((u >> 12) & 0x7ffu);
+  return max((s << 15) | v, 1u);
+}
+
+// Selection order of a tie record (rec = key << 32 | position): the key,
+// then the lower position.
 __device__ __forceinline__ unsigned long long tie_composite(unsigned long long rec) {
-  // rec = key << 32 | position
-  return composite52(make_uint4((uint32_t)(rec >> 32), (uint32_t)rec, 0u, 0u));
+  return rec ^ 0xffffffffull;
 }
 
 __device__ __forceinline__ unsigned long long to_fixed(float w) {
@@ -351,6 +376,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   int32_t* frows = a.ws.rows + (size_t)bh * d.cap;
 
   // ======================================================= phase 1: LUT and scan
+  // one round's codes and positions (-1: past the cluster)
   auto issue = [&](FRound<G, PT>& r, int base, int e1) {
 #pragma unroll
     for (int t = 0; t < PT; ++t) {
@@ -362,66 +388,92 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       }
     }
   };
-  // the wave's first round goes out before the tables are built, after the
-  // tables' own loads (which need no index offsets)
+  // the same for the first round, where lanes past the cluster load its
+  // first entry (or entry 0) instead, so that every thread issues the same
+  // loads in phase 1 and the waits on them are exact
+  auto issue_all = [&](FRound<G, PT>& r, int base, int e1) {
+#pragma unroll
+    for (int t = 0; t < PT; ++t) {
+      const int e = base + t * 64 + lane;
+      const int el = e < e1 ? e : min(base, max(d.cap - 1, 0));
+      r.cw[t] = codes[el];
+      r.pp[t] = pos[el];
+      if (e >= e1) r.pp[t] = -1;
+    }
+  };
+  // the wave's first round goes out before the tables are built
   int c = c0 + wave;
   int e0 = 0, e1 = 0;
   FRound<G, PT> rb[2];
   {
-    // LUT[m][j][g] = scale*log2e * q_g^(m) . B_m[j].  Every thread's codebook
-    // rows are loaded at once (codeword j = tid % 256, subspaces tid / 256 +
-    // step * i), while q is staged in LDS as scaled floats; then the dot
-    // products run from registers and LDS.
-    constexpr int kPairs = kM * kKsub / NT;
-    constexpr int kMStep = NT / kKsub;
-    static_assert(kPairs * NT == kM * kKsub && kMStep >= 1, "LUT pairs");
-    const int j = tid & (kKsub - 1), m0 = tid / kKsub;
-    float4 cb[kPairs][2];
+    // LUT[m][j][g] = scale*log2e * q_g^(m) . B_m[j].  Thread t computes the
+    // entries of subspace m = t / 32 for codewords j = t % 32 + 32 i: its
+    // q^(m) of the G heads stays in registers, and the lanes of a half wave
+    // read consecutive codebook rows.  Loads go out in the order they are
+    // needed (they complete in issue order, and every thread issues the same
+    // ones): q, then the codebook rows and the first centroids, then the
+    // scan's first round (the cluster offsets are scalar loads).
+    constexpr int kTPM = NT / kM;           // threads per subspace
+    constexpr int kPer = kKsub / kTPM;      // codewords per thread
+    static_assert(kTPM * kM == NT && kPer * kTPM == kKsub, "LUT split");
+    const int lm = tid / kTPM, lj = tid % kTPM;
+    const int l16r = tid & 15;
+    // q of the G heads, packed bf16: subspace lm (LUT) and dims l16r*8.. (QC)
+    uint4 qlw[G], qcw[G];
 #pragma unroll
-    for (int i = 0; i < kPairs; ++i) {
-      const float* cw = a.ix.codebooks + (((size_t)bh * kM + m0 + kMStep * i) * kKsub + j) * kDsub;
+    for (int g = 0; g < G; ++g) {
+      qlw[g] = *reinterpret_cast<const uint4*>(qh + g * kD + lm * kDsub);
+      qcw[g] = *reinterpret_cast<const uint4*>(qh + g * kD + l16r * 8);
+    }
+    if (c < c1) {
+      e0 = entry_at(c);
+      e1 = max(e0, entry_at(c + 1));
+    }
+    float4 cb[kPer][2];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const float* cw =
+          a.ix.codebooks + (((size_t)bh * kM + lm) * kKsub + lj + kTPM * i) * kDsub;
       cb[i][0] = *reinterpret_cast<const float4*>(cw);
       cb[i][1] = *reinterpret_cast<const float4*>(cw + 4);
     }
     // the first cluster of this thread's 16-lane row for the QC pass
-    const int l16r = tid & 15;
-    float4 cen0 = make_float4(0.f, 0.f, 0.f, 0.f), cen1 = cen0;
-    if ((tid >> 4) < ncl) {
-      const float* cp = cent + (size_t)(c0 + (tid >> 4)) * kD + l16r * 8;
+    float4 cen0, cen1;
+    {
+      const int cl0 = min(c0 + min(tid >> 4, max(ncl - 1, 0)), d.L - 1);
+      const float* cp = cent + (size_t)cl0 * kD + l16r * 8;
       cen0 = *reinterpret_cast<const float4*>(cp);
       cen1 = *reinterpret_cast<const float4*>(cp + 4);
     }
-    uint4 qw = make_uint4(0, 0, 0, 0);
-    if (tid < G * kD / 8) qw = *reinterpret_cast<const uint4*>(qh + tid * 8);
-    if (c < c1) {
-      e0 = entry_at(c);
-      e1 = max(e0, entry_at(c + 1));
-      issue(rb[0], e0, e1);
-    }
-    float* qsl = reinterpret_cast<float*>(hist);   // scaled q [G][128] until the QC pass
-    if (tid < G * kD / 8) {
-      const uint4 w = qw;
-      const float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+    issue_all(rb[0], e0, e1);
+    // keep every load above in flight before any of them is used (the
+    // scheduler would otherwise sink the codebook loads into the loop below,
+    // one memory round trip per piece)
+    __builtin_amdgcn_sched_barrier(0);
+    // the scaled q values, as the staged table kernel forms them
+    auto scaled = [&](const uint4& w, float* f) {
+      const float v[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                           bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qsl[tid * 8 + i] = f[i] * d.scale_log2;
-    }
-    __syncthreads();
+      for (int i = 0; i < 8; ++i) f[i] = v[i] * d.scale_log2;
+    };
+    float qr[G][kDsub];
 #pragma unroll
-    for (int i = 0; i < kPairs; ++i) {
-      const int m = m0 + kMStep * i;
+    for (int g = 0; g < G; ++g) scaled(qlw[g], qr[g]);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int j = lj + kTPM * i;
       const float cv[8] = {cb[i][0].x, cb[i][0].y, cb[i][0].z, cb[i][0].w,
                            cb[i][1].x, cb[i][1].y, cb[i][1].z, cb[i][1].w};
       float outv[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float* qq = qsl + g * kD + m * kDsub;
-        float sacc = qq[0] * cv[0];
+        float sacc = qr[g][0] * cv[0];
 #pragma unroll
-        for (int t = 1; t < kDsub; ++t) sacc = fmaf(qq[t], cv[t], sacc);
+        for (int t = 1; t < kDsub; ++t) sacc = fmaf(qr[g][t], cv[t], sacc);
         outv[g] = sacc;
       }
-      float* dst = lut + (m * kKsub + j) * G;
+      float* dst = lut + (lm * kKsub + j) * G;
       if constexpr (G == 8) {
         reinterpret_cast<float4*>(dst)[0] = make_float4(outv[0], outv[1], outv[2], outv[3]);
         reinterpret_cast<float4*>(dst)[1] = make_float4(outv[4], outv[5], outv[6], outv[7]);
@@ -446,7 +498,8 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       float qcv[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float* qq = qsl + g * kD + l16r * 8;
+        float qq[8];
+        scaled(qcw[g], qq);
         float sacc = qq[0] * cv[0];
 #pragma unroll
         for (int t = 1; t < 8; ++t) sacc = fmaf(qq[t], cv[t], sacc);
@@ -460,12 +513,12 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
         }
       }
     }
-    __syncthreads();   // the staged q is read for the last time above
     for (int i = tid; i < kHistBins; i += NT) hist[i] = 0u;
     for (int i = tid; i < ncl * G; i += NT) wsel[i] = 0ull;
     if (tid == 0) S.nextc = c0 + NW;
   }
-  __syncthreads();
+  // LDS only: the scan's first round stays in flight
+  lds_sync();
   float qc[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) qc[g] = c < c1 ? qcl[(c - c0) * G + g] : 0.0f;
@@ -511,14 +564,14 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
         float kappa = v[0];
 #pragma unroll
         for (int g = 1; g < G; ++g) kappa = fmaxf(kappa, v[g]);
-        uint32_t key = 0;
+        uint32_t code = 0;
         if (p >= si.cand_beg && p < si.cand_end) {
-          key = order_key(kappa);
-          atomicAdd(&hist[key >> (32 - kHistBits)], 1u);
+          code = key_code16(order_key(kappa));
+          atomicAdd(&hist[code >> (16 - kHistBits)], 1u);
 #pragma unroll
           for (int g = 0; g < G; ++g) s[t][g] = v[g];
         }
-        keys[e] = (uint16_t)(key >> 16);
+        keys[e] = (uint16_t)code;
       }
     }
 #pragma unroll
@@ -563,7 +616,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     if (!(c < c1)) break;
     round(rb[1], rb[0]);
   }
-  __syncthreads();
+  lds_sync();
   // The block's own threshold bucket beta_b: at least k of its keys lie in
   // bins >= beta_b, so the head's threshold bucket is >= beta_b and the bins
   // below cannot matter.  Only bins >= beta_b go to the head's histogram
@@ -573,7 +626,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   // with fewer than k candidates of its own the block flushes every bin, and
   // the head's threshold may lie below its bins: it then reads them all
   const int read_lo = S.res[2] >= si.k ? beta_b : 0;
-  __syncthreads();
+  lds_sync();
   if (beta_b >= 0) {
     for (int i = beta_b + tid; i < kHistBins; i += NT) {
       const uint32_t v = hist[i];
@@ -598,10 +651,10 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   int beta = -1;
   if (beta_b >= 0) {
     for (int i = read_lo + tid; i < kHistBins; i += NT) hist[i] = ld_dev(&ghist[i]);
-    __syncthreads();
+    lds_sync();
     block_threshold<NT>(hist, read_lo, si.k, S.res, S.sh);
     beta = S.res[0];
-    __syncthreads();
+    lds_sync();
   }
   const bool any = beta >= 0;
   auto entry_w = [&](int e, int cl, float* w, uint32_t* key) {
@@ -650,14 +703,14 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     }
   };
   auto record_list = [&]() {
-    __syncthreads();
+    lds_sync();
     for (int li = tid; li < la + lt; li += NT) {
       const bool isA = li < la;
       if (isA) record(elist[li], true, na - la + li);
       else record(elist[kListCap - 1 - (li - la)], false, nt - lt + (li - la));
     }
     la = lt = 0;
-    __syncthreads();
+    lds_sync();
   };
   if (any && E1 - E0 <= kChunk) {
     // one chunk (the keys already in pk): list, then record
@@ -682,7 +735,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       if (li < kListCap) elist[li] = e;
       else record(e, isA, isA ? li : li - ta);
     }
-    __syncthreads();
+    lds_sync();
     for (int li = tid; li < min(ta + tt, kListCap); li += NT) {
       const bool isA = li < ta;
       record(elist[li], isA, isA ? li : li - ta);
@@ -776,7 +829,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     }
     if (tid == 63) { S.apre[P] = xa; S.tpre[P] = xt; }
   }
-  __syncthreads();
+  lds_sync();
   const int n_above = S.apre[P], n_tie = S.tpre[P];
   const int ksel = min(si.k, n_above + n_tie);
   const int r = max(ksel - n_above, 0);
@@ -831,27 +884,41 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     }
     frows[rr] = p;
   }
-  __syncthreads();
+  lds_sync();
+  // the r winners of the bucket: the composites >= the r-th largest
+  // (prefix under mask)
   unsigned long long prefix = 0, mask = 0;
   const bool all = r >= n_tie;
-  if (r > 0 && !all) {
+  if (r > 0 && !all && cached && n_tie <= kRankMax) {
+    // few ties: each one counts the ties above it; the one with r - 1 above
+    // is the r-th largest (composites are distinct: positions are)
+    for (int i = tid; i < n_tie; i += NT) {
+      const unsigned long long ci = tie_composite(tcache[i]);
+      int above = 0;
+      for (int j = 0; j < n_tie; ++j) above += tie_composite(tcache[j]) > ci;
+      if (above == r - 1) S.thr = ci;
+    }
+    lds_sync();
+    prefix = S.thr;
+    mask = ~0ull;
+  } else if (r > 0 && !all) {
+    // many ties: radix select, 8 bits at a time from the top
     int need = r;
-    for (int shift = 44;; shift -= 8) {
-      const int s = shift > 0 ? shift : 0;
-      const unsigned long long dm = shift >= 0 ? 0xffull : 0xfull;
+    for (int s = 56;; s -= 8) {
+      constexpr unsigned long long dm = 0xffull;
       for (int i = tid; i < 256; i += NT) S.rh[i] = 0;
-      __syncthreads();
+      lds_sync();
       for (int i = tid; i < n_tie; i += NT) {
         const unsigned long long cp = tie_composite(tie_rec(i));
         if ((cp & mask) == prefix) atomicAdd(&S.rh[(cp >> s) & dm], 1u);
       }
-      __syncthreads();
+      lds_sync();
       if (tid < 64) {
         int v4[4], sl = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int bin = 255 - (tid * 4 + i);
-          v4[i] = bin <= (int)dm ? (int)S.rh[bin] : 0;
+          v4[i] = (int)S.rh[bin];
           sl += v4[i];
         }
         const int x = wave_incl_scan(sl);
@@ -868,13 +935,13 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
           }
         }
       }
-      __syncthreads();
+      lds_sync();
       const int dig = S.res[0];
       need -= S.res[1];
       prefix |= (unsigned long long)dig << s;
       mask |= dm << s;
       const bool done = S.res[2] == need || s == 0;
-      __syncthreads();
+      lds_sync();
       if (done) break;
     }
   }
@@ -919,7 +986,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       run += tw;
     }
   }
-  __syncthreads();
+  lds_sync();
   // background logits of the block's clusters: log2 of the unselected weight
   // (relative to the cluster max) plus the max
   float* sbg = reinterpret_cast<float*>(hist);
@@ -977,7 +1044,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
         }
       }
     }
-    __syncthreads();
+    lds_sync();
     auto load_item = [&](int j, uint4& kw, uint4& vw) {
       kw = vw = make_uint4(0, 0, 0, 0);
       if (j < n) {

@@ -246,12 +246,43 @@ def test_tables_and_keys_match_oracle(staged):
             got = bits.view(np.float32).astype(np.float64)
             np.testing.assert_allclose(got, kap[p[iscand]], atol=2e-5, rtol=2e-6)
         else:
-            # the reference key of the fp32-rounded value, top 16 bits: equal,
-            # or one apart where fp32 rounding crosses a 16-bit boundary
+            # the 16-bit code of the fp32-rounded reference key: equal, or one
+            # apart where fp32 rounding crosses a code boundary
             x = kap[p[iscand]].astype(np.float32).view(np.uint32)
-            ref = np.where(x & 0x80000000, ~x, x | 0x80000000).astype(np.uint32) >> 16
+            ref = key_code16(np.where(x & 0x80000000, ~x, x | 0x80000000).astype(np.uint32))
             assert np.all(f > 0)
             assert np.abs(f.astype(np.int64) - ref.astype(np.int64)).max() <= 1
+
+
+def key_code16(u):
+    """The fused step's 16-bit key code of order keys u (uint32 array): sign,
+    binary exponent clamped to the 16 binades [2^-7, 2^9) (the same field range
+    in both halves of the order key), 11 mantissa bits; at least 1."""
+    u = np.asarray(u, np.uint32).astype(np.int64)
+    s = u >> 31
+    f = (u >> 23) & 0xFF
+    lo = 127 - 7
+    v = ((f - lo) << 11) | ((u >> 12) & 0x7FF)
+    v = np.where(f < lo, 0, np.where(f > lo + 15, 0x7FFF, v))
+    return np.maximum((s << 15) | v, 1)
+
+
+def test_key_code16_is_monotone():
+    # every pair of neighbouring floats keeps its order (or shares a code),
+    # across both signs, zeros, the window's edges and infinities
+    vals = np.concatenate([np.float32([-np.inf, -3e38, -1e3, -512.0, -511.9, -2.0 ** -7,
+                                       -1e-3, -0.0, 0.0, 1e-30, 2.0 ** -7, 3.49, 3.5, 511.9,
+                                       512.0, 1e30, np.inf]),
+                           np.linspace(-600, 600, 100001, dtype=np.float32),
+                           np.float32(np.random.default_rng(3).standard_normal(10000) * 50)])
+    vals = np.sort(vals)
+    x = vals.view(np.uint32)
+    u = np.where(x & 0x80000000, ~x, x | 0x80000000).astype(np.uint32)
+    c = key_code16(u)
+    assert np.all(np.diff(c) >= 0) and c.min() >= 1 and c.max() <= 0xFFFF
+    # inside the window a code spans 1/2048 of a binade
+    w = (np.abs(vals) >= 2.0 ** -7) & (np.abs(vals) < 512)
+    assert np.unique(c[w]).size > 0.5 * np.unique(vals[w]).size
 
 
 def test_default_and_staged_paths_agree():
