@@ -765,7 +765,10 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       int oa, ot, ta, tt;
       block_scan2<NT>(ca, ct, &oa, &ot, &ta, &tt, S.sh);
       const bool fits = ta + tt <= kListCap;
-      if (fits && la + lt + ta + tt > kListCap) record_list();
+      // the listed entries are recorded at the last slots counted so far: a
+      // chunk that is recorded directly (or would overflow the list) goes
+      // after them, so they are recorded first
+      if (la + lt > 0 && (!fits || la + lt + ta + tt > kListCap)) record_list();
       uint32_t chosen = chosenA | chosenT;
       while (chosen) {
         const int u = __ffs(chosen) - 1;

@@ -17,6 +17,7 @@ def _need_gpu():
 
 from gpu_helpers import (check_output, check_result, log, oracle_with_details,  # noqa: E402
                          parity, run_gpu)
+from key_codes import key_code16  # noqa: E402
 from pqhsa_synth import make_step_inputs  # noqa: E402
 
 
@@ -31,6 +32,17 @@ def test_dense_matches_oracle(T, G, Hkv):
     g = run_gpu(inp, dense=True)
     ref = oracle.dense_step(inp)
     check_output(g["O"], ref, f"dense T={T}")
+
+
+@pytest.mark.parametrize("wid", [2, 4])
+def test_dense_full_size_matches_oracle(wid):
+    # the dense split-K step at the 128K and 512K layer shapes, in the launch
+    # configuration the benchmark times, every query head against the oracle
+    import oracle
+    inp = make_step_inputs(wid)
+    log(f"[dense] workload {wid} full size")
+    g = run_gpu(inp, dense=True)
+    check_output(g["O"], oracle.dense_step(inp), f"dense workload {wid}")
 
 
 def test_dense_variable_lengths_and_spare_pages():
@@ -254,37 +266,6 @@ def test_tables_and_keys_match_oracle(staged):
             assert np.abs(f.astype(np.int64) - ref.astype(np.int64)).max() <= 1
 
 
-def key_code16(u):
-    """The fused step's 16-bit key code of order keys u (uint32 array): sign,
-    binary exponent clamped to the 16 binades [2^-7, 2^9) (the same field range
-    in both halves of the order key), 11 mantissa bits; at least 1."""
-    u = np.asarray(u, np.uint32).astype(np.int64)
-    s = u >> 31
-    f = (u >> 23) & 0xFF
-    lo = 127 - 7
-    v = ((f - lo) << 11) | ((u >> 12) & 0x7FF)
-    v = np.where(f < lo, 0, np.where(f > lo + 15, 0x7FFF, v))
-    return np.maximum((s << 15) | v, 1)
-
-
-def test_key_code16_is_monotone():
-    # every pair of neighbouring floats keeps its order (or shares a code),
-    # across both signs, zeros, the window's edges and infinities
-    vals = np.concatenate([np.float32([-np.inf, -3e38, -1e3, -512.0, -511.9, -2.0 ** -7,
-                                       -1e-3, -0.0, 0.0, 1e-30, 2.0 ** -7, 3.49, 3.5, 511.9,
-                                       512.0, 1e30, np.inf]),
-                           np.linspace(-600, 600, 100001, dtype=np.float32),
-                           np.float32(np.random.default_rng(3).standard_normal(10000) * 50)])
-    vals = np.sort(vals)
-    x = vals.view(np.uint32)
-    u = np.where(x & 0x80000000, ~x, x | 0x80000000).astype(np.uint32)
-    c = key_code16(u)
-    assert np.all(np.diff(c) >= 0) and c.min() >= 1 and c.max() <= 0xFFFF
-    # inside the window a code spans 1/2048 of a binade
-    w = (np.abs(vals) >= 2.0 ** -7) & (np.abs(vals) < 512)
-    assert np.unique(c[w]).size > 0.5 * np.unique(vals[w]).size
-
-
 def test_default_and_staged_paths_agree():
     # same tables in the same order: identical keys, so identical selections;
     # outputs differ only by summation order
@@ -386,10 +367,10 @@ def test_full_budget_long_context_few_clusters():
 @pytest.mark.parametrize("budget_bp", [2500, 6000])
 def test_many_key_chunks_per_block(budget_bp):
     # 2 clusters over 64K tokens: 2 blocks of 32K entries, four key chunks
-    # each.  At 25 % the chosen entries of two or three chunks fill the
-    # block's list, which a later chunk records before listing its own; at
-    # 60 % every chunk chooses more than the list holds and records its own
-    # entries
+    # each.  At 25 % some chunks' chosen entries fit the block's list and
+    # others are recorded directly, so a listed chunk must be recorded before
+    # a later chunk is recorded at the slots after it; at 60 % every chunk
+    # chooses more than the list holds and records its own entries
     inp = make_step_inputs(0, context_lens=[65536], num_lists=2, budget_bp=budget_bp,
                            workload_id=18)
     log(f"[pqhsa] budget {budget_bp} bp at 64K over 2 clusters")
