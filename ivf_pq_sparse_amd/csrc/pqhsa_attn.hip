@@ -344,6 +344,141 @@ __device__ void background_block(const StepArgs& a, int bh, int split, AttendLds
   block_merge_store<G>(sh, part_base, d.n_parts, d.n_exact_splits + split);
 }
 
+// ---------------------------------------------------------------- dense split-K on MFMA
+// Dense decode attention of one (b, h), split over the context: the head's
+// W = 4 * splits waves (4 per block) take its pages (16 tokens each) in turn,
+// wave w the pages w, w + W, w + 2W, ..., so that at any moment the head's
+// waves read neighbouring pages, and with every head progressing alike the
+// heads' rows of a page (interleaved in the cache) are read at about the same
+// time.  Each wave keeps the next page's K and V in flight while it computes
+// the current:
+//   logits:  S^T[16 tok][16 cols] = K[16 tok][128] . Q^T[128][16 cols], four
+//            16x16x32 bf16 MFMAs (cols = the G query heads, the rest zero);
+//            lane l holds S[tok 4(l/16) + i][col l%16], i = 0..3
+//   softmax: per column a running base-2 maximum, raised only when a page's
+//            maximum exceeds it by more than 8 (weights stay below 2^8);
+//            lane l's four weights are exactly the B operand of
+//   values:  O^T[128][16 cols] += V^T[128][16 tok] . P^T[16 tok][16 cols],
+//            32 16x16x4 fp32 MFMAs (products and sums in fp32): for token
+//            group i and dim offset c, lane l supplies V[tok 4(l/16) + i]
+//            [8(l%16) + c] (its 16-byte load of that row) and accumulates
+//            O[col l%16][dims 32(l/16) + 8i' + c], i' = 0..3.
+// K is read in 64-byte runs per lane, V in whole 256-byte rows per 16 lanes.
+// The block merges its four waves into one partial per query head.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+template <int G>
+__global__ __launch_bounds__(256) void k_dense_mfma(StepArgs a) {
+  __shared__ AttendLds<G> sh;
+  const Dims& d = a.d;
+  const int BH = d.B * d.Hkv;
+  int bh, split;
+  xcd_map(blockIdx.x, BH, d.n_exact_splits, &bh, &split);
+  const int b = bh / d.Hkv, h = bh % d.Hkv;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, j = lane >> 4;
+  const int T = min(max(a.ctx[b], 0), d.cap);
+  const int n_tiles = (T + kPage - 1) / kPage;
+  const int t1 = n_tiles;
+  const int nwh = d.n_exact_splits * 4;   // waves of the head
+  // Q^T: for MFMA c, lane l holds q[col][32j + 8c .. +8] (zero past the G heads)
+  bf16x8 qb[4];
+  {
+    const uint16_t* q = a.q + ((size_t)b * d.Hq + h * G + min(col, G - 1)) * kD + 32 * j;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 w = *reinterpret_cast<const uint4*>(q + 8 * c);
+      if (col >= G) w = make_uint4(0, 0, 0, 0);
+      qb[c] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  const int32_t* tab = a.table + (size_t)b * d.max_pages;
+  const size_t rstride = (size_t)d.Hkv * kD;   // elements between a page's token rows
+  // a tile's loads: K[slot col][32j .. 32j + 32) and V[slot 4j + i][8 col .. + 8]
+  auto load_tile = [&](int tile, uint4 (&kb)[4], uint4 (&vb)[4]) {
+    const int page = min(max(tab[tile], 0), d.num_pages - 1);
+    const uint16_t* kr = a.kc + ((size_t)page * kPage + col) * rstride + (size_t)h * kD + 32 * j;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kb[c] = *reinterpret_cast<const uint4*>(kr + 8 * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      vb[i] = *reinterpret_cast<const uint4*>(
+          a.vc + ((size_t)page * kPage + 4 * j + i) * rstride + (size_t)h * kD + 8 * col);
+  };
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 kb[2][4], vb[2][4];
+  int tile = split * 4 + wave;
+  if (tile < t1) load_tile(tile, kb[0], vb[0]);
+  auto step = [&](uint4 (&kc)[4], uint4 (&vc)[4], uint4 (&kn)[4], uint4 (&vn)[4]) {
+    const int next = tile + nwh;
+    if (next < t1) load_tile(next, kn, vn);
+    f32x4 sv = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[c]), qb[c], sv,
+                                                   0, 0, 0);
+    const int tok0 = tile * kPage + 4 * j;
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = tok0 + i < T ? sv[i] * d.scale_log2 : -INFINITY;
+    float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    if (__any(mt > m_run + 8.0f)) {
+      // raise the column's reference maximum (uniform over its four lanes);
+      // a wave-wide vote keeps the lane exchange off the common path
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      if (mt > m_run + 8.0f) {
+        const float al = __builtin_amdgcn_exp2f(m_run - mt);
+        l_run *= al;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] *= al;
+        m_run = mt;
+      }
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(s[i] - m_run);
+      l_run += p[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 w = tok0 + i < T ? vc[i] : make_uint4(0, 0, 0, 0);
+      const float v[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                          bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[c], p[i], acc[c], 0, 0, 0);
+    }
+    tile = next;
+  };
+  while (tile < t1) {
+    step(kb[0], vb[0], kb[1], vb[1]);
+    if (tile >= t1) break;
+    step(kb[1], vb[1], kb[0], vb[0]);
+  }
+  // the column's sum over its four lanes; the wave's state to LDS
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (col < G) {
+    if (j == 0) {
+      sh.ml[wave][col][0] = m_run;
+      sh.ml[wave][col][1] = l_run;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sh.acc[wave][col][32 * j + 8 * i + c] = acc[c][i];
+  }
+  float* part_base = a.ws.partials + ((size_t)b * d.Hq + h * G) * d.n_parts * kPart;
+  block_merge_store<G>(sh, part_base, d.n_parts, split);
+}
+
 // One launch for both: blocks [0, BH*n_exact) do split-K, the rest background.
 template <int G, int SRC>
 __global__ __launch_bounds__(256) void k_attend(StepArgs a) {
@@ -449,8 +584,7 @@ template <int G>
 static hipError_t attend_g(const StepArgs& a, bool dense, const Launch& l) {
   const int BH = a.d.B * a.d.Hkv;
   if (dense)
-    return launch_kernel(k_attend<G, kRowsDense>, dim3(BH * a.d.n_exact_splits), dim3(256), 0, l,
-                         a);
+    return launch_kernel(k_dense_mfma<G>, dim3(BH * a.d.n_exact_splits), dim3(256), 0, l, a);
   return launch_kernel(k_attend<G, kRowsIndex>, dim3(BH * (a.d.n_exact_splits + a.d.n_bg_splits)),
                        dim3(256), 0, l, a);
 }
