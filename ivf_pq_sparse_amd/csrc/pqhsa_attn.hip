@@ -7,23 +7,21 @@
 // paragraphs); unread tokens contribute their approximate weight summed per
 // cluster times the cluster mean (fifth paragraph).  The merge is the
 // prefix/suffix law O = (N_P + N_S)/(D_P + D_S) of the quant_prune_distill
-// post on query reuse, over all partials.  Dense and sparse modes share the
-// split-K kernel, as the activation/KV-sparsity crossover article (rit.work
+// post on query reuse, over all partials.  Dense and sparse exact attention
+// run through the same row-tile MFMA code (pqhsa_internal.hpp: tile_logits,
+// tile_accumulate), as the activation/KV-sparsity crossover article (rit.work
 // blog, section "Why one method gives different speed-ups") requires of an
-// honest baseline.  The same split-K kernel also serves query reuse: each
-// query head starts at the context length of the earlier query whose prefix
-// state it reuses (0 when it reuses none), and the reused state joins the
-// merge as one more partial.
+// honest baseline: the dense step's tiles are the pages of the context, the
+// sparse steps' tiles are gathered from their row lists.  The same code also
+// serves query reuse: each query head starts at the context length of the
+// earlier query whose prefix state it reuses (0 when it reuses none), and the
+// reused state joins the merge as one more partial.
 //
-// Split-K block: 256 threads = 16 row groups of 16 lanes (one DPP row each).
-// The block first stages the cache offsets of up to 256 rows in LDS (row list
-// and block table read once, in parallel); each row group then streams its
-// rows with the next two rows' K and V (16 B per lane, 256 B per row) in
-// flight while it computes the current two: the G dot products use a 16-lane
-// DPP reduction, and an online base-2 softmax (max, sum, acc[8 dims]) is kept
-// per query head.  Row groups of a wave merge through lane shuffles, the 4
-// waves through LDS, and the block writes one partial (m, l, acc[128]) per
-// query head.
+// Split-K block: 4 waves.  The block stages the cache offsets of up to 256
+// rows in LDS (row list and block table read once, in parallel); wave w takes
+// the staged row tiles w, w + 4, ... with the next tile's K and V in flight.
+// The 4 waves merge through LDS and the block writes one partial
+// (m, l, acc[128]) per query head.
 #include "pqhsa_internal.hpp"
 
 namespace pqhsa {
@@ -42,7 +40,6 @@ struct AttendLds {
 // Where the rows of a split-K block come from.
 enum RowSource {
   kRowsIndex = 0,   // the step's exact-row list (sink, selected, recent)
-  kRowsDense = 1,   // the whole context [0, T)
   kRowsReuse = 2    // [start_g, T) per query head g, after the reuse decision
 };
 
@@ -112,6 +109,23 @@ __device__ void block_merge_store(AttendLds<G>& sh, float* part_base, int n_part
   }
 }
 
+// A wave's row-tile state into the block's LDS slot `wave`.
+template <int G>
+__device__ void tile_state_to_lds(const RowTileState& st, int wave, int col, int j,
+                                  AttendLds<G>& sh) {
+  if (col < G) {
+    if (j == 0) {
+      sh.ml[wave][col][0] = st.m;
+      sh.ml[wave][col][1] = st.l;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sh.acc[wave][col][32 * j + 8 * i + c] = st.acc[c][i];
+  }
+}
+
+
 // Split-K exact attention for one (b, h, split): its share of the rows of the
 // source SRC (see RowSource).  With kRowsReuse the rows [base, T) (base the
 // smallest start of the G heads) go to splits of equal size (at least
@@ -123,8 +137,6 @@ template <int G, int SRC>
 __device__ void exact_block(const StepArgs& a, int bh, int split, AttendLds<G>& sh) {
   const Dims& d = a.d;
   const int b = bh / d.Hkv, h = bh % d.Hkv;
-  const int l16 = threadIdx.x & 15;
-  const int rg = threadIdx.x >> 4;
   int n_rows, base = 0, split_rows = 0;
   int s0[G] = {};
   if constexpr (SRC == kRowsIndex) {
@@ -170,39 +182,25 @@ __device__ void exact_block(const StepArgs& a, int bh, int split, AttendLds<G>& 
     r0 = base + min(n_rows, split * chunk);
     r1 = base + min(n_rows, split * chunk + chunk);
   }
-  // heads that take row `p` (all of them unless some reuse a prefix)
-  auto act = [&](int p) -> uint32_t {
-    if constexpr (SRC != kRowsReuse) return 0xffu;
-    uint32_t m = 0;
+  // row tiles: the rows of a phase are staged as cache offsets in LDS; wave
+  // w takes the phase's tiles w, w + 4, ..., the next tile's loads in flight
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15, j = lane >> 4;
+  // the first position this lane's column (query head) attends to: a head
+  // that reuses a prefix starts after it
+  int start = 0;
+  if constexpr (SRC == kRowsReuse) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) m |= (uint32_t)(p >= s0[g]) << g;
-    return m;
-  };
-
-  float qv[G][8];
-  {
-    const uint16_t* q = a.q + ((size_t)b * d.Hq + h * G) * kD + l16 * 8;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint4 w = *reinterpret_cast<const uint4*>(q + g * kD);
-      const float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                          bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qv[g][i] = f[i] * d.scale_log2;
-    }
+    for (int g = 0; g < G; ++g)
+      if (col == g) start = s0[g];
   }
-  AttnState<G> st;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    st.m[g] = -INFINITY;
-    st.l[g] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.acc[g][i] = 0.0f;
-  }
+  bf16x8 qb[4];
+  tile_query<G>(a.q + ((size_t)b * d.Hq + h * G) * kD, col, j, qb);
+  RowTileState st;
+  tile_init(st);
   const int32_t* tab = a.table + (size_t)b * d.max_pages;
   const int32_t* rows = a.ws.rows + (size_t)bh * d.cap;
-  const uint16_t* kc = a.kc + l16 * 8;
-  const uint16_t* vc = a.vc + l16 * 8;
   for (int ph = r0; ph < r1; ph += kPhaseRows) {
     const int n = min(kPhaseRows, r1 - ph);
     if ((int)threadIdx.x < n) {
@@ -214,63 +212,55 @@ __device__ void exact_block(const StepArgs& a, int bh, int split, AttendLds<G>& 
           ((long long)(page * kPage + (p & (kPage - 1))) * d.Hkv + h) * kD;
     }
     __syncthreads();
-    // rows j and j + 16 of the group per pair; two pairs' buffers alternate
-    // (the loop is unrolled by two so that no buffer is copied), the next
-    // pair's loads in flight while a pair is computed.  A row past the
-    // phase's end loads the phase's last row instead (finite values, weight
-    // zero), so that no register needs clearing.
-    auto load_pair = [&](int j, uint4 (&kv)[4]) {
+    const int nt = (n + 15) / 16;
+    // K[row col] 64 bytes at 32j, V[row 4j + i] 16 bytes at 8 col; rows past
+    // the phase load nothing
+    auto load_tile = [&](int t, uint4 (&kb)[4], uint4 (&vb)[4]) {
+      const int rk = 16 * t + col;
+      if (rk < n) {
+        const uint16_t* kr = a.kc + sh.row_off[rk] + 32 * j;
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const long long o = sh.row_off[min(j + 16 * r, n - 1)];
-        kv[2 * r] = *reinterpret_cast<const uint4*>(kc + o);
-        kv[2 * r + 1] = *reinterpret_cast<const uint4*>(vc + o);
+        for (int c = 0; c < 4; ++c) kb[c] = *reinterpret_cast<const uint4*>(kr + 8 * c);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kb[c] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rv = 16 * t + 4 * j + i;
+        vb[i] = rv < n ? *reinterpret_cast<const uint4*>(a.vc + sh.row_off[rv] + 8 * col)
+                       : make_uint4(0, 0, 0, 0);
       }
     };
-    auto run_pair = [&](int j, const uint4 (&kv)[4]) {
-      attend_rows2<G>(st, qv, kv[0], kv[1], kv[2], kv[3], act(ph + j),
-                      j + 16 < n ? act(ph + j + 16) : 0u);
+    uint4 kb[2][4], vb[2][4];
+    int t = wave;
+    if (t < nt) load_tile(t, kb[0], vb[0]);
+    auto step = [&](uint4 (&kc)[4], uint4 (&vc)[4], uint4 (&kn)[4], uint4 (&vn)[4]) {
+      if (t + 4 < nt) load_tile(t + 4, kn, vn);
+      const f32x4 sv = tile_logits(qb, kc, d.scale_log2);
+      float s[4], v[4][8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rv = 16 * t + 4 * j + i;
+        // the logit of row 4j + i for query head `col`: kept if the head
+        // takes the row (past its reused prefix, if any); the V slice
+        // (dims 8 col ..) serves every head, rows past the phase hold zeros
+        const bool ok = rv < n && (SRC != kRowsReuse || ph + rv >= start);
+        s[i] = ok ? sv[i] : -INFINITY;
+        bf16x8_to_f32(vc[i], v[i]);
+      }
+      tile_accumulate(st, s, v);
+      t += 4;
     };
-    uint4 pa[4], pb[4];
-    int j = rg;
-    if (j < n) load_pair(j, pa);
-    while (j < n) {
-      if (j + 32 < n) load_pair(j + 32, pb);
-      run_pair(j, pa);
-      if (j + 32 >= n) break;
-      if (j + 64 < n) load_pair(j + 64, pa);
-      run_pair(j + 32, pb);
-      j += 64;
+    while (t < nt) {
+      step(kb[0], vb[0], kb[1], vb[1]);
+      if (t >= nt) break;
+      step(kb[1], vb[1], kb[0], vb[0]);
     }
     __syncthreads();
   }
-  // merge the wave's 4 row groups (lanes l, l^16, l^32, l^48 hold the same dims)
-#pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(st.m[g], o);
-      const float lo = __shfl_xor(st.l[g], o);
-      float M, a0, a1;
-      lse_factors(st.m[g], mo, &M, &a0, &a1);
-      st.l[g] = st.l[g] * a0 + lo * a1;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float ao = __shfl_xor(st.acc[g][i], o);
-        st.acc[g][i] = st.acc[g][i] * a0 + ao * a1;
-      }
-      st.m[g] = M;
-    }
-  }
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) < 16) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (l16 == 0) { sh.ml[wave][g][0] = st.m[g]; sh.ml[wave][g][1] = st.l[g]; }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sh.acc[wave][g][l16 * 8 + i] = st.acc[g][i];
-    }
-  }
+  tile_finish(st);
+  tile_state_to_lds<G>(st, wave, col, j, sh);
   float* part_base = a.ws.partials + ((size_t)b * d.Hq + h * G) * d.n_parts * kPart;
   block_merge_store<G>(sh, part_base, d.n_parts, split);
 }
@@ -344,30 +334,16 @@ __device__ void background_block(const StepArgs& a, int bh, int split, AttendLds
   block_merge_store<G>(sh, part_base, d.n_parts, d.n_exact_splits + split);
 }
 
-// ---------------------------------------------------------------- dense split-K on MFMA
+// ---------------------------------------------------------------- dense split-K
 // Dense decode attention of one (b, h), split over the context: the head's
-// W = 4 * splits waves (4 per block) take its pages (16 tokens each) in turn,
-// wave w the pages w, w + W, w + 2W, ..., so that at any moment the head's
-// waves read neighbouring pages, and with every head progressing alike the
-// heads' rows of a page (interleaved in the cache) are read at about the same
-// time.  Each wave keeps the next page's K and V in flight while it computes
-// the current:
-//   logits:  S^T[16 tok][16 cols] = K[16 tok][128] . Q^T[128][16 cols], four
-//            16x16x32 bf16 MFMAs (cols = the G query heads, the rest zero);
-//            lane l holds S[tok 4(l/16) + i][col l%16], i = 0..3
-//   softmax: per column a running base-2 maximum, raised only when a page's
-//            maximum exceeds it by more than 8 (weights stay below 2^8);
-//            lane l's four weights are exactly the B operand of
-//   values:  O^T[128][16 cols] += V^T[128][16 tok] . P^T[16 tok][16 cols],
-//            32 16x16x4 fp32 MFMAs (products and sums in fp32): for token
-//            group i and dim offset c, lane l supplies V[tok 4(l/16) + i]
-//            [8(l%16) + c] (its 16-byte load of that row) and accumulates
-//            O[col l%16][dims 32(l/16) + 8i' + c], i' = 0..3.
-// K is read in 64-byte runs per lane, V in whole 256-byte rows per 16 lanes.
-// The block merges its four waves into one partial per query head.
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-
+// W = 4 * splits waves (4 per block) take its pages (16 tokens each, one row
+// tile) in turn, wave w the pages w, w + W, w + 2W, ..., so that at any moment
+// the head's waves read neighbouring pages, and with every head progressing
+// alike the heads' rows of a page (interleaved in the cache) are read at about
+// the same time.  Each wave keeps the next page's K and V in flight while the
+// row-tile MFMAs compute the current; K is read in 64-byte runs per lane, V in
+// whole 256-byte rows per 16 lanes.  The block merges its four waves into one
+// partial per query head.
 template <int G>
 __global__ __launch_bounds__(256) void k_dense_mfma(StepArgs a) {
   __shared__ AttendLds<G> sh;
@@ -381,22 +357,12 @@ __global__ __launch_bounds__(256) void k_dense_mfma(StepArgs a) {
   const int col = lane & 15, j = lane >> 4;
   const int T = min(max(a.ctx[b], 0), d.cap);
   const int n_tiles = (T + kPage - 1) / kPage;
-  const int t1 = n_tiles;
   const int nwh = d.n_exact_splits * 4;   // waves of the head
-  // Q^T: for MFMA c, lane l holds q[col][32j + 8c .. +8] (zero past the G heads)
   bf16x8 qb[4];
-  {
-    const uint16_t* q = a.q + ((size_t)b * d.Hq + h * G + min(col, G - 1)) * kD + 32 * j;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint4 w = *reinterpret_cast<const uint4*>(q + 8 * c);
-      if (col >= G) w = make_uint4(0, 0, 0, 0);
-      qb[c] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
+  tile_query<G>(a.q + ((size_t)b * d.Hq + h * G) * kD, col, j, qb);
   const int32_t* tab = a.table + (size_t)b * d.max_pages;
   const size_t rstride = (size_t)d.Hkv * kD;   // elements between a page's token rows
-  // a tile's loads: K[slot col][32j .. 32j + 32) and V[slot 4j + i][8 col .. + 8]
+  // a page's loads: K[slot col][32j .. 32j + 32) and V[slot 4j + i][8 col .. + 8]
   auto load_tile = [&](int tile, uint4 (&kb)[4], uint4 (&vb)[4]) {
     const int page = min(max(tab[tile], 0), d.num_pages - 1);
     const uint16_t* kr = a.kc + ((size_t)page * kPage + col) * rstride + (size_t)h * kD + 32 * j;
@@ -407,74 +373,34 @@ __global__ __launch_bounds__(256) void k_dense_mfma(StepArgs a) {
       vb[i] = *reinterpret_cast<const uint4*>(
           a.vc + ((size_t)page * kPage + 4 * j + i) * rstride + (size_t)h * kD + 8 * col);
   };
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x4 acc[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  RowTileState st;
+  tile_init(st);
   uint4 kb[2][4], vb[2][4];
   int tile = split * 4 + wave;
-  if (tile < t1) load_tile(tile, kb[0], vb[0]);
+  if (tile < n_tiles) load_tile(tile, kb[0], vb[0]);
   auto step = [&](uint4 (&kc)[4], uint4 (&vc)[4], uint4 (&kn)[4], uint4 (&vn)[4]) {
     const int next = tile + nwh;
-    if (next < t1) load_tile(next, kn, vn);
-    f32x4 sv = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[c]), qb[c], sv,
-                                                   0, 0, 0);
+    if (next < n_tiles) load_tile(next, kn, vn);
+    const f32x4 sv = tile_logits(qb, kc, d.scale_log2);
     const int tok0 = tile * kPage + 4 * j;
-    float s[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = tok0 + i < T ? sv[i] * d.scale_log2 : -INFINITY;
-    float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    if (__any(mt > m_run + 8.0f)) {
-      // raise the column's reference maximum (uniform over its four lanes);
-      // a wave-wide vote keeps the lane exchange off the common path
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      if (mt > m_run + 8.0f) {
-        const float al = __builtin_amdgcn_exp2f(m_run - mt);
-        l_run *= al;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] *= al;
-        m_run = mt;
-      }
-    }
-    float p[4];
+    float s[4], v[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(s[i] - m_run);
-      l_run += p[i];
+      // rows past the context hold whatever the page does
+      const bool ok = tok0 + i < T;
+      s[i] = ok ? sv[i] : -INFINITY;
+      bf16x8_to_f32(ok ? vc[i] : make_uint4(0, 0, 0, 0), v[i]);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 w = tok0 + i < T ? vc[i] : make_uint4(0, 0, 0, 0);
-      const float v[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                          bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[c], p[i], acc[c], 0, 0, 0);
-    }
+    tile_accumulate(st, s, v);
     tile = next;
   };
-  while (tile < t1) {
+  while (tile < n_tiles) {
     step(kb[0], vb[0], kb[1], vb[1]);
-    if (tile >= t1) break;
+    if (tile >= n_tiles) break;
     step(kb[1], vb[1], kb[0], vb[0]);
   }
-  // the column's sum over its four lanes; the wave's state to LDS
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (col < G) {
-    if (j == 0) {
-      sh.ml[wave][col][0] = m_run;
-      sh.ml[wave][col][1] = l_run;
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sh.acc[wave][col][32 * j + 8 * i + c] = acc[c][i];
-  }
+  tile_finish(st);
+  tile_state_to_lds<G>(st, wave, col, j, sh);
   float* part_base = a.ws.partials + ((size_t)b * d.Hq + h * G) * d.n_parts * kPart;
   block_merge_store<G>(sh, part_base, d.n_parts, split);
 }
@@ -555,8 +481,9 @@ __global__ __launch_bounds__(256) void k_merge(StepArgs a) {
   __syncthreads();
   if (half == 0) {
     const float tot = sum + half1[dim];
-    a.out[(size_t)bq * kD + dim] = L > 0.0f ? tot / L : 0.0f;
-    if (dim == 0 && a.lse) a.lse[bq] = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+    // no rows at all: O = 0, lse = -inf; a NaN sum stays NaN (never hidden)
+    a.out[(size_t)bq * kD + dim] = L != 0.0f ? tot / L : 0.0f;
+    if (dim == 0 && a.lse) a.lse[bq] = L != 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
     if (a.ru.st) {
       // query reuse: this step's state goes into the head's ring
       const int w = (int)((uint32_t)a.ru.cnt[bq] % (uint32_t)a.ru.W);

@@ -1180,8 +1180,9 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
         for (int j = 0; j < kMaxFusedP; ++j) A = fmaf(fg[j], x[j], A);
         const float M = mlh[g * 2], L = mlh[g * 2 + 1];
         const size_t bq = (size_t)b * d.Hq + h * G + g;
-        float o = L > 0.0f ? A / L : 0.0f;
-        float ls = L > 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+        // no rows at all: O = 0, lse = -inf; a NaN sum stays NaN
+        float o = L != 0.0f ? A / L : 0.0f;
+        float ls = L != 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
         if (timed_out) o = ls = __builtin_nanf("");
         a.out[bq * kD + dim] = o;
         if (dim == 0 && a.lse) a.lse[bq] = ls;

@@ -539,6 +539,115 @@ __device__ __forceinline__ void attend_rows2(AttnState<G>& st, const float (&qv)
   }
 }
 
+// ---------------------------------------------------------------- row tiles on MFMA
+// Every exact-attention path (the dense step, the exact rows and background
+// terms of the sparse steps, query reuse) accumulates through these.  A wave
+// takes tiles of 16 rows (cache rows, or background terms with a given logit
+// and value) for the 16 columns of its query heads (G of them used):
+//   logits:  S^T[16 rows][16 cols] = K[16 rows][128] . Q^T[128][16 cols],
+//            four 16x16x32 bf16 MFMAs; lane l holds S[row 4(l/16) + i][col
+//            l%16], i = 0..3, and supplies K[row l%16][32(l/16) + 8c .. + 8]
+//            to MFMA c (with q[col][32(l/16) + 8c .. + 8] as its B operand)
+//   softmax: per column a running base-2 maximum, raised only when a tile's
+//            maximum exceeds it by more than 8 (weights stay below 2^8); the
+//            lane's four weights are exactly the B operand of
+//   values:  O^T[128][16 cols] += V^T[128][16 rows] . P^T[16 rows][16 cols],
+//            32 16x16x4 fp32 MFMAs (products and sums in fp32): for row group
+//            i and dim offset c, lane l supplies the value of row 4(l/16) + i
+//            at dim 8(l%16) + c and accumulates O[col l%16][32(l/16) + 8i' + c]
+//            in acc[c][i'], i' = 0..3.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+struct RowTileState {
+  float m;        // base-2 reference maximum of the lane's column
+  float l;        // sum of the lane's rows' weights against m
+  f32x4 acc[8];   // O[col][32j + 8i + c] in acc[c][i], unnormalised
+};
+
+// Reference maximum of a column that has taken no row yet: finite, so that a
+// masked row (logit -inf) weighs exp2(-inf) = 0 rather than exp2(NaN) even
+// in a tile where every row of the column is masked; the first real logit
+// raises it; tile_finish maps a column that took none to the empty state.
+constexpr float kTileMInit = -1.0e30f;
+
+__device__ __forceinline__ void tile_init(RowTileState& st) {
+  st.m = kTileMInit;
+  st.l = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) st.acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// B operand of the logit MFMAs: lane (col, j) holds q[col][32j + 8c .. + 8]
+// for MFMA c, zero for columns past the G query heads (q: bf16 [G][128]).
+template <int G>
+__device__ __forceinline__ void tile_query(const uint16_t* q, int col, int j, bf16x8 (&qb)[4]) {
+  const uint16_t* qr = q + min(col, G - 1) * kD + 32 * j;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint4 w = *reinterpret_cast<const uint4*>(qr + 8 * c);
+    if (col >= G) w = make_uint4(0, 0, 0, 0);
+    qb[c] = __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+// Base-2 logits of a tile of cache rows for the lane's column: kb[c] as
+// described above (zero for rows that are not there); sv[i] is row 4j + i.
+__device__ __forceinline__ f32x4 tile_logits(const bf16x8 (&qb)[4], const uint4 (&kb)[4],
+                                             float scale_log2) {
+  f32x4 sv = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[c]), qb[c], sv, 0,
+                                                 0, 0);
+  return sv * scale_log2;
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(uint4 w, float (&v)[8]) {
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+
+// One tile into the state: s[i] is the base-2 logit of row 4j + i for the
+// lane's column (-inf: no row), v[i][c] its value at dim 8 col + c (finite,
+// 0 where there is no row, so that a zero weight never meets a NaN).
+__device__ __forceinline__ void tile_accumulate(RowTileState& st, const float (&s)[4],
+                                                const float (&v)[4][8]) {
+  float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  if (__any(mt > st.m + 8.0f)) {
+    // raise the column's reference maximum (uniform over its four lanes); a
+    // wave-wide vote keeps the lane exchange off the common path
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    if (mt > st.m + 8.0f) {
+      const float al = __builtin_amdgcn_exp2f(st.m - mt);
+      st.l *= al;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) st.acc[c] *= al;
+      st.m = mt;
+    }
+  }
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(s[i] - st.m);
+    st.l += p[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[i][c], p[i], st.acc[c], 0, 0, 0);
+}
+
+// After the last tile: l summed over the column's four lanes, and the
+// maximum of a column that took no row set to -inf (the empty state).
+__device__ __forceinline__ void tile_finish(RowTileState& st) {
+  st.l += __shfl_xor(st.l, 16);
+  st.l += __shfl_xor(st.l, 32);
+  if (st.l == 0.0f) st.m = -INFINITY;
+}
+
 // Scale factors that bring states with maxima m0 and m1 to their common max.
 __device__ __forceinline__ void lse_factors(float m0, float m1, float* M, float* a0, float* a1) {
   *M = fmaxf(m0, m1);
