@@ -24,12 +24,13 @@
 //            it are selected, those inside it are published as ties; the
 //            selected entries' weights are added to per-cluster sums.
 //   barrier  (counts and records complete)
-//   phase 3  every block resolves the tie bucket with the same radix select
-//            (52-bit composite: low key bits, then inverted position, so equal
-//            keys prefer the lower position), takes an even share of the exact
-//            rows (sink, selected, recent/tail) plus its own clusters'
-//            background terms, and writes one partial (m, l, acc[128]) per
-//            query head.  The last block of the head to finish merges the P
+//   phase 3  every block resolves the tie bucket alike (64-bit composite:
+//            the full key, then the inverted position, so equal keys prefer
+//            the lower position; rank counting for a few ties, a radix select
+//            for many), takes an even share of the exact rows (sink, selected,
+//            recent/tail) plus its own clusters' background terms, attends
+//            them in the 16-row MFMA tiles of the dense step, and writes one
+//            partial (m, l, acc[128]) per query head.  The last block of the head to finish merges the P
 //            partials into O and the log-sum-exp, writes the ascending selected
 //            positions if asked, and clears the head's counters and histogram
 //            for the next step.
@@ -59,9 +60,6 @@ template <int G>
 struct FusedCfg {
   static constexpr int NT = 512;   // 8 waves: up to 256 VGPRs each
   static constexpr int NW = NT / 64;
-  static constexpr int NG = NT / 16;                // 16-lane row groups
-  static constexpr int kItemsPerGroup = 4;
-  static constexpr int kItems = NG * kItemsPerGroup;   // attention items staged per phase
   static constexpr size_t kUBytes = (size_t)kM * kKsub * G * sizeof(float);   // LUT, then reuse
   static constexpr size_t kHBytes = (size_t)kHistBins * sizeof(uint32_t);
   // clusters x G per block whose per-cluster values live in LDS (smaller at
@@ -72,8 +70,6 @@ struct FusedCfg {
   static constexpr size_t kBBytes = (size_t)kCG * 2 * sizeof(float);            // cluster (max, sum)
   static constexpr size_t kDyn = kUBytes + kHBytes + kWBytes + kQBytes + kBBytes;
   static constexpr int kTieCap = (int)(kUBytes / sizeof(unsigned long long));
-  static_assert((size_t)NW * G * (2 + kD) * sizeof(float) <= kUBytes, "merge arrays");
-  static_assert((size_t)kItems * sizeof(long long) + 4096 <= kHBytes, "item staging");
 };
 
 constexpr int kRankMax = 512;   // threshold-bucket ties resolved by counting ranks
@@ -261,58 +257,6 @@ __device__ __forceinline__ unsigned long long to_fixed(float w) {
   return (unsigned long long)(w * kFixScale + 0.5f);
 }
 
-// One background item: the cluster's summed unselected weight as a logit
-// s_g (base 2) and its mean value as the row's value (8 dims per lane).
-template <int G>
-__device__ __forceinline__ void attend_bg(AttnState<G>& st, const float* sg, uint4 m0, uint4 m1) {
-  const float mu[8] = {__uint_as_float(m0.x), __uint_as_float(m0.y), __uint_as_float(m0.z),
-                       __uint_as_float(m0.w), __uint_as_float(m1.x), __uint_as_float(m1.y),
-                       __uint_as_float(m1.z), __uint_as_float(m1.w)};
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float s = sg[g];
-    if (s == -INFINITY) continue;
-    const float mn = fmaxf(st.m[g], s);
-    const float al = __builtin_amdgcn_exp2f(st.m[g] - mn);
-    const float p = __builtin_amdgcn_exp2f(s - mn);
-    st.l[g] = fmaf(st.l[g], al, p);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.acc[g][i] = fmaf(st.acc[g][i], al, p * mu[i]);
-    st.m[g] = mn;
-  }
-}
-
-// One exact row for the G query heads, with q kept as packed bf16 (the
-// scale is applied to the row sum).
-template <int G>
-__device__ __forceinline__ void attend_row_pk(AttnState<G>& st, const uint4 (&qp)[G], float scl,
-                                              uint4 kw, uint4 vw) {
-  const float kf[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
-                       bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
-  const float vf[8] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y),
-                       bf16_lo(vw.z), bf16_hi(vw.z), bf16_lo(vw.w), bf16_hi(vw.w)};
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint4 q = qp[g];
-    float s = bf16_lo(q.x) * kf[0];
-    s = fmaf(bf16_hi(q.x), kf[1], s);
-    s = fmaf(bf16_lo(q.y), kf[2], s);
-    s = fmaf(bf16_hi(q.y), kf[3], s);
-    s = fmaf(bf16_lo(q.z), kf[4], s);
-    s = fmaf(bf16_hi(q.z), kf[5], s);
-    s = fmaf(bf16_lo(q.w), kf[6], s);
-    s = fmaf(bf16_hi(q.w), kf[7], s);
-    s = row16_sum(s) * scl;
-    const float mn = fmaxf(st.m[g], s);
-    const float al = __builtin_amdgcn_exp2f(st.m[g] - mn);
-    const float p = __builtin_amdgcn_exp2f(s - mn);
-    st.l[g] = fmaf(st.l[g], al, p);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.acc[g][i] = fmaf(st.acc[g][i], al, p * vf[i]);
-    st.m[g] = mn;
-  }
-}
-
 template <int G, int PT>
 struct FRound {
   uint4 cw[PT];
@@ -324,9 +268,8 @@ struct FRound {
 template <int G>
 __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   using C = FusedCfg<G>;
-  constexpr int NT = C::NT, NW = C::NW, NG = C::NG;
+  constexpr int NT = C::NT, NW = C::NW;
   constexpr int PT = 5;   // 64-entry tiles per scan round (most clusters in one)
-  constexpr int kIB = G == 8 ? 2 : 4;  // attention items whose loads are in flight together
   extern __shared__ __align__(16) unsigned char dyn[];
   __shared__ FusedStatic S;
   float* lut = reinterpret_cast<float*>(dyn);
@@ -807,11 +750,11 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   barrier_wait(&sync[kSyncStride], nbar, a.ws.fflags, hflag, d.fbar_ticks, last2);
 
   // ======================================================= phase 3: ties, rows, partials
-  // the queries for the exact rows (packed bf16, 8 dims per lane of a 16-lane
-  // row), loaded now so that their latency is hidden
-  uint4 qp[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) qp[g] = *reinterpret_cast<const uint4*>(qh + g * kD + (tid & 15) * 8);
+  // the queries as the row tiles' B operand, loaded now so that their latency
+  // is hidden
+  const int tcol = lane & 15, tj = lane >> 4;
+  bf16x8 qb[4];
+  tile_query<G>(qh, tcol, tj, qb);
   if (tid < 64) {
     unsigned long long v = 0;
     int jb = 0, je = 0;   // block tid's entries [jb, je)
@@ -1000,28 +943,27 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     const float wb = binl[((cl - c0) * G + g) * 2 + 1] - (float)wsel[i] * kFixInv;
     sbg[i] = (wb > 0.0f && M != -INFINITY) ? M + log2f(wb) : -INFINITY;
   }
-  // exact rows and background clusters as one item list through 16-lane groups
-  const int l16 = tid & 15, rg = tid >> 4;
-  AttnState<G> st;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    st.m[g] = -INFINITY;
-    st.l[g] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.acc[g][i] = 0.0f;
-  }
+  // Exact rows and background clusters in 16-row tiles (the row-tile MFMAs of
+  // the dense and staged steps): the exact rows of a phase are staged as
+  // cache offsets in LDS, up to kStage at a time; the phase's tiles are its
+  // exact-row tiles followed, in the last phase, by the background tiles,
+  // whose rows are clusters with a given logit per query head and the
+  // cluster mean as value.  Wave w takes tiles w, w + NW, ... with the next
+  // tile's loads in flight.  Every tile issues the same 8 loads per lane
+  // (rows past the end load a valid row with weight zero), so that the waits
+  // on them are exact.
+  RowTileState st;
+  tile_init(st);
   const int nr = hi - lo;
-  const int n_items = nr + (d.exact_only ? 0 : ncl);   // background items last
+  const int nbg = d.exact_only ? 0 : ncl;
+  const int nbt = (nbg + 15) / 16;
   const int32_t* tab = a.table + (size_t)b * d.max_pages;
-  const uint16_t* kc = a.kc + l16 * 8;
-  const uint16_t* vc = a.vc + l16 * 8;
-  const float* means = a.ix.means + (size_t)bh * d.L * kD + l16 * 8;
-  // Items are staged up to kStage at a time (their cache offsets in LDS); a
-  // 16-lane group takes items rg, rg + NG, ... in that order, with the loads
-  // of the next kIB of them in flight while it computes.
+  const float* means = a.ix.means + ((size_t)bh * d.L + c0) * kD;
   constexpr int kStage = (int)((C::kHBytes - 4096) / sizeof(long long));
-  for (int ph = 0; ph < n_items; ph += kStage) {
-    const int n = min(kStage, n_items - ph);
+  const int n_ph = max(1, (nr + kStage - 1) / kStage);
+  for (int phi = 0; phi < n_ph; ++phi) {
+    const int ph = phi * kStage;
+    const int n = max(0, min(kStage, nr - ph));
     __syncthreads();
     {
       // a thread's rows, then their pages, each round of loads issued at once
@@ -1029,100 +971,121 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       int pr[kPerT], pg[kPerT];
 #pragma unroll
       for (int i = 0; i < kPerT; ++i) {
-        const int t = tid + i * NT, it = ph + t;
-        pr[i] = (t < n && it < nr) ? min(max(frows[lo + it], 0), d.cap - 1) : -1;
+        const int t = tid + i * NT;
+        pr[i] = t < n ? min(max(frows[lo + ph + t], 0), d.cap - 1) : -1;
       }
 #pragma unroll
       for (int i = 0; i < kPerT; ++i) pg[i] = pr[i] >= 0 ? tab[pr[i] >> 4] : 0;
 #pragma unroll
       for (int i = 0; i < kPerT; ++i) {
-        const int t = tid + i * NT, it = ph + t;
+        const int t = tid + i * NT;
         if (t < n) {
-          if (it < nr) {
-            const int page = min(max(pg[i], 0), d.num_pages - 1);
-            ioff[t] = ((long long)(page * kPage + (pr[i] & (kPage - 1))) * d.Hkv + h) * kD;
-          } else {
-            ioff[t] = -1 - (long long)(it - nr);
-          }
+          const int page = min(max(pg[i], 0), d.num_pages - 1);
+          ioff[t] = ((long long)(page * kPage + (pr[i] & (kPage - 1))) * d.Hkv + h) * kD;
         }
       }
     }
     lds_sync();
-    auto load_item = [&](int j, uint4& kw, uint4& vw) {
-      kw = vw = make_uint4(0, 0, 0, 0);
-      if (j < n) {
-        const long long o = ioff[j];
-        if (o >= 0) {
-          kw = *reinterpret_cast<const uint4*>(kc + o);
-          vw = *reinterpret_cast<const uint4*>(vc + o);
-        } else {
-          const float* mu = means + (size_t)(c0 + (int)(-1 - o)) * kD;
-          kw = *reinterpret_cast<const uint4*>(mu);
-          vw = *reinterpret_cast<const uint4*>(mu + 4);
+    const int net = (n + 15) / 16;
+    const int ntl = net + (phi == n_ph - 1 ? nbt : 0);
+    // exact tile: K[row col] 64 B at 32j in bf[0..3], V[row 4j + i] 16 B at
+    // 8 col in bf[4 + i]; background tile: the means of clusters 4j + i, 32 B
+    // at 8 col, in bf[2i], bf[2i + 1]
+    auto load_tile = [&](int t, uint4 (&bf)[8]) {
+      if (t < net) {
+        const uint16_t* kr = a.kc + ioff[min(16 * t + tcol, n - 1)] + 32 * tj;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bf[c] = *reinterpret_cast<const uint4*>(kr + 8 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          bf[4 + i] = *reinterpret_cast<const uint4*>(
+              a.vc + ioff[min(16 * t + 4 * tj + i, n - 1)] + 8 * tcol);
+      } else {
+        const int cb = 16 * (t - net) + 4 * tj;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float* mu = means + (size_t)min(cb + i, nbg - 1) * kD + 8 * tcol;
+          bf[2 * i] = *reinterpret_cast<const uint4*>(mu);
+          bf[2 * i + 1] = *reinterpret_cast<const uint4*>(mu + 4);
         }
       }
     };
-    uint4 kw[kIB], vw[kIB];
+    uint4 bf[2][8];
+    int t = wave;
+    if (t < ntl) load_tile(t, bf[0]);
+    auto step = [&](uint4 (&cur)[8], uint4 (&nxt)[8]) {
+      if (t + NW < ntl) load_tile(t + NW, nxt);
+      float sv[4], v[4][8];
+      if (t < net) {
+        const f32x4 lg = tile_logits(qb, *reinterpret_cast<const uint4(*)[4]>(&cur[0]),
+                                     d.scale_log2);
 #pragma unroll
-    for (int u = 0; u < kIB; ++u) load_item(rg + u * NG, kw[u], vw[u]);
-    for (int j0 = rg; j0 < n; j0 += kIB * NG) {
-#pragma unroll
-      for (int u = 0; u < kIB; ++u) {
-        const int j = j0 + u * NG;
-        if (j < n) {
-          const long long o = ioff[j];
-          if (o >= 0) attend_row_pk<G>(st, qp, d.scale_log2, kw[u], vw[u]);
-          else attend_bg<G>(st, sbg + (int)(-1 - o) * G, kw[u], vw[u]);
+        for (int i = 0; i < 4; ++i) {
+          sv[i] = 16 * t + 4 * tj + i < n ? lg[i] : -INFINITY;
+          bf16x8_to_f32(cur[4 + i], v[i]);
         }
-        load_item(j + kIB * NG, kw[u], vw[u]);
+      } else {
+        const int cb = 16 * (t - net) + 4 * tj;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[i] = (cb + i < nbg && tcol < G) ? sbg[(cb + i) * G + min(tcol, G - 1)] : -INFINITY;
+          const uint4 m0 = cur[2 * i], m1 = cur[2 * i + 1];
+          v[i][0] = __uint_as_float(m0.x); v[i][1] = __uint_as_float(m0.y);
+          v[i][2] = __uint_as_float(m0.z); v[i][3] = __uint_as_float(m0.w);
+          v[i][4] = __uint_as_float(m1.x); v[i][5] = __uint_as_float(m1.y);
+          v[i][6] = __uint_as_float(m1.z); v[i][7] = __uint_as_float(m1.w);
+        }
       }
+      tile_accumulate(st, sv, v);
+      t += NW;
+    };
+    while (t < ntl) {
+      step(bf[0], bf[1]);
+      if (t >= ntl) break;
+      step(bf[1], bf[0]);
     }
   }
+  tile_finish(st);
   __syncthreads();
-  // Block merge: every row group's state goes to LDS; the weight of each
-  // (row group, head) against the head's max is computed once; then each
-  // thread sums one output (head, dim) over the row groups.
-  static_assert(NG == 32 && (size_t)NG * G * kD * sizeof(float) <= C::kUBytes, "row states");
-  float* accr = reinterpret_cast<float*>(dyn);           // [NG][G][128]
-  float* mlr = reinterpret_cast<float*>(hist);           // [NG][G][2]
-  float* fr = mlr + NG * G * 2;                          // [G][NG]
-  float* mlg = fr + G * NG;                              // [G][2] head max and sum
+  // Block merge: the waves' states go to LDS; each thread then forms one
+  // output (head, dim) over the NW waves.
+  constexpr int kAS = kD + 4;   // padded row of a wave's accumulator
+  static_assert((size_t)NW * G * (kAS + 2) * sizeof(float) <= C::kUBytes, "wave states");
+  float* accw = reinterpret_cast<float*>(dyn);   // [NW][G][kAS]
+  float* mlw = accw + NW * G * kAS;              // [NW][G][2]
+  if (tcol < G) {
+    float* row = accw + (wave * G + tcol) * kAS + 32 * tj;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if (l16 == 0) {
-      mlr[(rg * G + g) * 2] = st.m[g];
-      mlr[(rg * G + g) * 2 + 1] = st.l[g];
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<float4*>(row + 8 * i) =
+          make_float4(st.acc[0][i], st.acc[1][i], st.acc[2][i], st.acc[3][i]);
+      *reinterpret_cast<float4*>(row + 8 * i + 4) =
+          make_float4(st.acc[4][i], st.acc[5][i], st.acc[6][i], st.acc[7][i]);
     }
-    float4* dst = reinterpret_cast<float4*>(accr + ((size_t)rg * G + g) * kD + l16 * 8);
-    dst[0] = make_float4(st.acc[g][0], st.acc[g][1], st.acc[g][2], st.acc[g][3]);
-    dst[1] = make_float4(st.acc[g][4], st.acc[g][5], st.acc[g][6], st.acc[g][7]);
-  }
-  __syncthreads();
-  if (tid < G * NG) {
-    // one 32-lane half wave per head
-    const int g = tid / NG, r = tid % NG;
-    const float m = mlr[(r * G + g) * 2];
-    float M = m;
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-    fr[g * NG + r] = f;
-    float L = f * mlr[(r * G + g) * 2 + 1];
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-    if (r == 0) { mlg[g * 2] = M; mlg[g * 2 + 1] = L; }
+    if (tj == 0) {
+      mlw[(wave * G + tcol) * 2] = st.m;
+      mlw[(wave * G + tcol) * 2 + 1] = st.l;
+    }
   }
   __syncthreads();
   for (int idx = tid; idx < G * kD; idx += NT) {
     const int g = idx / kD, dim = idx % kD;
-    float A = 0.0f;
-#pragma unroll 8
-    for (int r = 0; r < NG; ++r) A = fmaf(fr[g * NG + r], accr[((size_t)r * G + g) * kD + dim], A);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mlw[(w * G + g) * 2]);
+    float L = 0.0f, A = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float m = mlw[(w * G + g) * 2];
+      const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+      L = fmaf(f, mlw[(w * G + g) * 2 + 1], L);
+      A = fmaf(f, accw[(w * G + g) * kAS + dim], A);
+    }
     float* out = a.ws.fpart + (((size_t)bh * G + g) * kMaxFusedP + sub) * kPart;
     st_dev(&out[4 + dim], A);
     if (dim == 0) {
-      st_dev(&out[0], mlg[g * 2]);
-      st_dev(&out[1], mlg[g * 2 + 1]);
+      st_dev(&out[0], M);
+      st_dev(&out[1], L);
     }
   }
   wait_mem();

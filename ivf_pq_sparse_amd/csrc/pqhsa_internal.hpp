@@ -490,55 +490,6 @@ __device__ __forceinline__ int seg_of(const int* pre, int n, int i) {
   return lo;
 }
 
-// ---------------------------------------------------------------- attention helpers
-template <int G>
-struct AttnState {
-  float m[G], l[G], acc[G][8];
-};
-
-// Two K/V rows into the online softmax at once: one rescale of the state per
-// pair of rows (one exp2 and one multiply per accumulator fewer than two
-// single-row updates).  Head g takes row 0 (1) when bit g of act0 (act1) is
-// set.
-template <int G>
-__device__ __forceinline__ void attend_rows2(AttnState<G>& st, const float (&qv)[G][8],
-                                             uint4 kw0, uint4 vw0, uint4 kw1, uint4 vw1,
-                                             uint32_t act0, uint32_t act1) {
-  const float k0[8] = {bf16_lo(kw0.x), bf16_hi(kw0.x), bf16_lo(kw0.y), bf16_hi(kw0.y),
-                       bf16_lo(kw0.z), bf16_hi(kw0.z), bf16_lo(kw0.w), bf16_hi(kw0.w)};
-  const float k1[8] = {bf16_lo(kw1.x), bf16_hi(kw1.x), bf16_lo(kw1.y), bf16_hi(kw1.y),
-                       bf16_lo(kw1.z), bf16_hi(kw1.z), bf16_lo(kw1.w), bf16_hi(kw1.w)};
-  const float v0[8] = {bf16_lo(vw0.x), bf16_hi(vw0.x), bf16_lo(vw0.y), bf16_hi(vw0.y),
-                       bf16_lo(vw0.z), bf16_hi(vw0.z), bf16_lo(vw0.w), bf16_hi(vw0.w)};
-  const float v1[8] = {bf16_lo(vw1.x), bf16_hi(vw1.x), bf16_lo(vw1.y), bf16_hi(vw1.y),
-                       bf16_lo(vw1.z), bf16_hi(vw1.z), bf16_lo(vw1.w), bf16_hi(vw1.w)};
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float s0 = qv[g][0] * k0[0], s1 = qv[g][0] * k1[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) {
-      s0 = fmaf(qv[g][i], k0[i], s0);
-      s1 = fmaf(qv[g][i], k1[i], s1);
-    }
-    s0 = row16_sum(s0);
-    s1 = row16_sum(s1);
-    const bool a0 = act0 & (1u << g), a1 = act1 & (1u << g);
-    if (a0 || a1) {
-      const float t0 = a0 ? s0 : -INFINITY, t1 = a1 ? s1 : -INFINITY;
-      const float mn = fmaxf(st.m[g], fmaxf(t0, t1));
-      // the hardware exp2 (results below 2^-126 flush to zero: weights that
-      // small against the running maximum do not change the sums)
-      const float al = __builtin_amdgcn_exp2f(st.m[g] - mn);
-      const float p0 = __builtin_amdgcn_exp2f(t0 - mn), p1 = __builtin_amdgcn_exp2f(t1 - mn);
-      st.l[g] = fmaf(st.l[g], al, p0 + p1);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        st.acc[g][i] = fmaf(p1, v1[i], fmaf(st.acc[g][i], al, p0 * v0[i]));
-      st.m[g] = mn;
-    }
-  }
-}
-
 // ---------------------------------------------------------------- row tiles on MFMA
 // Every exact-attention path (the dense step, the exact rows and background
 // terms of the sparse steps, query reuse) accumulates through these.  A wave
