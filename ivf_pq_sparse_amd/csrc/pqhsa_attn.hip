@@ -238,7 +238,7 @@ __device__ void exact_block(const StepArgs& a, int bh, int split, AttendLds<G>& 
     auto step = [&](uint4 (&kc)[4], uint4 (&vc)[4], uint4 (&kn)[4], uint4 (&vn)[4]) {
       if (t + 4 < nt) load_tile(t + 4, kn, vn);
       const f32x4 sv = tile_logits(qb, kc, d.scale_log2);
-      float s[4], v[4][8];
+      float s[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rv = 16 * t + 4 * j + i;
@@ -247,9 +247,8 @@ __device__ void exact_block(const StepArgs& a, int bh, int split, AttendLds<G>& 
         // (dims 8 col ..) serves every head, rows past the phase hold zeros
         const bool ok = rv < n && (SRC != kRowsReuse || ph + rv >= start);
         s[i] = ok ? sv[i] : -INFINITY;
-        bf16x8_to_f32(vc[i], v[i]);
       }
-      tile_accumulate(st, s, v);
+      tile_accumulate(st, s, vc);
       t += 4;
     };
     while (t < nt) {
@@ -391,7 +390,7 @@ __global__ __launch_bounds__(256) void k_dense_mfma(StepArgs a) {
       s[i] = ok ? sv[i] : -INFINITY;
       bf16x8_to_f32(ok ? vc[i] : make_uint4(0, 0, 0, 0), v[i]);
     }
-    tile_accumulate(st, s, v);
+    tile_accumulate_fp32mfma(st, s, v);
     tile = next;
   };
   while (tile < n_tiles) {

@@ -1015,17 +1015,16 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     if (t < ntl) load_tile(t, bf[0]);
     auto step = [&](uint4 (&cur)[8], uint4 (&nxt)[8]) {
       if (t + NW < ntl) load_tile(t + NW, nxt);
-      float sv[4], v[4][8];
+      float sv[4];
       if (t < net) {
         const f32x4 lg = tile_logits(qb, *reinterpret_cast<const uint4(*)[4]>(&cur[0]),
                                      d.scale_log2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[i] = 16 * t + 4 * tj + i < n ? lg[i] : -INFINITY;
-          bf16x8_to_f32(cur[4 + i], v[i]);
-        }
+        for (int i = 0; i < 4; ++i) sv[i] = 16 * t + 4 * tj + i < n ? lg[i] : -INFINITY;
+        tile_accumulate(st, sv, *reinterpret_cast<const uint4(*)[4]>(&cur[4]));
       } else {
         const int cb = 16 * (t - net) + 4 * tj;
+        float v[4][8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           sv[i] = (cb + i < nbg && tcol < G) ? sbg[(cb + i) * G + min(tcol, G - 1)] : -INFINITY;
@@ -1035,8 +1034,8 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
           v[i][4] = __uint_as_float(m1.x); v[i][5] = __uint_as_float(m1.y);
           v[i][6] = __uint_as_float(m1.z); v[i][7] = __uint_as_float(m1.w);
         }
+        tile_accumulate_f32(st, sv, v);
       }
-      tile_accumulate(st, sv, v);
       t += NW;
     };
     while (t < ntl) {

@@ -502,11 +502,13 @@ __device__ __forceinline__ int seg_of(const int* pre, int n, int i) {
 //   softmax: per column a running base-2 maximum, raised only when a tile's
 //            maximum exceeds it by more than 8 (weights stay below 2^8); the
 //            lane's four weights are exactly the B operand of
-//   values:  O^T[128][16 cols] += V^T[128][16 rows] . P^T[16 rows][16 cols],
-//            32 16x16x4 fp32 MFMAs (products and sums in fp32): for row group
-//            i and dim offset c, lane l supplies the value of row 4(l/16) + i
-//            at dim 8(l%16) + c and accumulates O[col l%16][32(l/16) + 8i' + c]
-//            in acc[c][i'], i' = 0..3.
+//   values:  O^T[128][16 cols] += V^T[128][16 rows] . P^T[16 rows][16 cols]
+//            as eight 16x16x32 bf16 MFMAs, one per dim offset c (the MFMA's
+//            row m stands for dim 8m + c): lane l supplies the bf16 values of
+//            rows 4(l/16) + i at dim 8(l%16) + c, each twice, against the
+//            weights split into a bf16 part and its bf16 residue (products
+//            exact to 2^-17, sums in fp32), and accumulates
+//            O[col l%16][32(l/16) + 8i' + c] in acc[c][i'], i' = 0..3.
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
@@ -554,16 +556,12 @@ __device__ __forceinline__ f32x4 tile_logits(const bf16x8 (&qb)[4], const uint4 
   return sv * scale_log2;
 }
 
-__device__ __forceinline__ void bf16x8_to_f32(uint4 w, float (&v)[8]) {
-  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
-}
-
-// One tile into the state: s[i] is the base-2 logit of row 4j + i for the
-// lane's column (-inf: no row), v[i][c] its value at dim 8 col + c (finite,
-// 0 where there is no row, so that a zero weight never meets a NaN).
-__device__ __forceinline__ void tile_accumulate(RowTileState& st, const float (&s)[4],
-                                                const float (&v)[4][8]) {
+// Online softmax of one tile: s[i] is the base-2 logit of row 4j + i for the
+// lane's column (-inf: no row); returns the rows' weights against the
+// column's reference maximum, which is raised (and the state rescaled) only
+// when the tile exceeds it by more than 8.
+__device__ __forceinline__ void tile_softmax(RowTileState& st, const float (&s)[4],
+                                             float (&p)[4]) {
   float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   if (__any(mt > st.m + 8.0f)) {
     // raise the column's reference maximum (uniform over its four lanes); a
@@ -578,17 +576,103 @@ __device__ __forceinline__ void tile_accumulate(RowTileState& st, const float (&
       st.m = mt;
     }
   }
-  float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     p[i] = __builtin_amdgcn_exp2f(s[i] - st.m);
     st.l += p[i];
   }
+}
+
+// x as a sum of two bf16 numbers, each rounded to nearest: |x - hi - lo| is
+// below 2^-17 |x|, and a product of either with a bf16 value is exact in fp32.
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
+}
+
+// B operand of the value MFMAs: the lane's four weights (rows 4j + i) at
+// k = 8j + i as bf16, their rounding residues at k = 8j + 4 + i.
+__device__ __forceinline__ bf16x8 tile_weights_operand(const float (&p)[4]) {
+  bf16x8 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __bf16 h, l;
+    split_bf16(p[i], h, l);
+    w[i] = h;
+    w[4 + i] = l;
+  }
+  return w;
+}
+
+// A operand of the value MFMA for dim offset c: element c of the lane's four
+// bf16 rows (8 values each), at k = 8j + i and again at 8j + 4 + i, so that
+// one MFMA takes both halves of the split weights.
+__device__ __forceinline__ bf16x8 tile_values_operand(const uint4 (&v)[4], int c) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = c < 2 ? v[i].x : c < 4 ? v[i].y : c < 6 ? v[i].z : v[i].w;
+    w[i] = (c & 1) ? x >> 16 : x & 0xffffu;
+  }
+  const uint32_t lo = w[0] | (w[1] << 16), hi = w[2] | (w[3] << 16);
+  return __builtin_bit_cast(bf16x8, make_uint4(lo, hi, lo, hi));
+}
+
+// One tile of bf16 rows into the state: v[i] holds row 4j + i at dims
+// 8 col .. 8 col + 7 (finite, so that a zero weight never meets a NaN).
+// Values are exact bf16 and the weights are split into two bf16 terms, so
+// the eight 16x16x32 bf16 MFMAs form every product to 2^-17 and sum in fp32.
+__device__ __forceinline__ void tile_accumulate(RowTileState& st, const float (&s)[4],
+                                                const uint4 (&v)[4]) {
+  float p[4];
+  tile_softmax(st, s, p);
+  const bf16x8 w = tile_weights_operand(p);
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tile_values_operand(v, c), w, st.acc[c],
+                                                       0, 0, 0);
+}
+
+// The same for fp32 values v[i][c] (row 4j + i, dim 8 col + c): each value
+// is split into two bf16 terms as well, one MFMA per term.
+__device__ __forceinline__ void tile_accumulate_f32(RowTileState& st, const float (&s)[4],
+                                                    const float (&v)[4][8]) {
+  float p[4];
+  tile_softmax(st, s, p);
+  const bf16x8 w = tile_weights_operand(p);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    bf16x8 vh, vl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __bf16 h, l;
+      split_bf16(v[i][c], h, l);
+      vh[i] = vh[4 + i] = h;
+      vl[i] = vl[4 + i] = l;
+    }
+    st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, w, st.acc[c], 0, 0, 0);
+    st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl, w, st.acc[c], 0, 0, 0);
+  }
+}
+
+// The same for fp32 values on 32 16x16x4 fp32 MFMAs (for row group i and
+// dim offset c, lane l supplies v[i][c] against its weight p[i]).  The dense
+// step uses this form: on its HBM-bound page loop it measured faster than the
+// split-weight bf16 form, although it issues more matrix work.
+__device__ __forceinline__ void tile_accumulate_fp32mfma(RowTileState& st, const float (&s)[4],
+                                                         const float (&v)[4][8]) {
+  float p[4];
+  tile_softmax(st, s, p);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int c = 0; c < 8; ++c)
       st.acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[i][c], p[i], st.acc[c], 0, 0, 0);
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(uint4 w, float (&v)[8]) {
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
 }
 
 // After the last tile: l summed over the column's four lanes, and the
