@@ -789,6 +789,49 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     return cached ? tcache[i] : ld_dev(&ftie[tie_slot(i)]);
   };
   const int own0 = S.tpre[sub];
+  // This block's rows of the head's exact list [sink | above | tie winners |
+  // recent]: every row but the winners is known already.  When the block's
+  // share fits one staging (and the cached ties leave room at the top of the
+  // LUT region), the rows go straight to LDS: the known rows' positions are
+  // loaded now, so that their latency overlaps the tie loads and the tie
+  // selection, and the winners are placed there by the selection; otherwise
+  // they go through the head's row list in the workspace.
+  const int n_rec = si.T - si.recent_beg;
+  const int R = si.ns + ksel + n_rec;
+  const int lo = (int)((long long)sub * R / P), hi = (int)((long long)(sub + 1) * R / P);
+  const int nr = hi - lo;
+  constexpr int kStage = (int)((C::kHBytes - 4096) / sizeof(long long));   // rows per staging
+  constexpr int kPerT = (kStage + NT - 1) / NT;
+  const size_t tie_bytes = (r > 0 && cached) ? (size_t)n_tie * sizeof(unsigned long long) : 0;
+  const bool direct =
+      nr <= kStage && tie_bytes + (size_t)kStage * (sizeof(long long) + sizeof(int32_t)) <= C::kUBytes;
+  long long* ioffd = reinterpret_cast<long long*>(dyn + C::kUBytes - (size_t)kStage * sizeof(long long));
+  int32_t* posd = reinterpret_cast<int32_t*>(ioffd) - kStage;   // winners' positions
+  auto known_pos = [&](int rr) -> int {   // -1 for a tie winner's row
+    if (rr < si.ns) return rr;
+    if (rr < si.ns + n_above) {
+      const int s = rr - si.ns;
+      const int j = seg_of(S.apre, P, s);
+      return ld_dev(&fpos[S.tbase[j] + (s - S.apre[j])]);
+    }
+    if (rr < si.ns + ksel) return -1;
+    return si.recent_beg + (rr - si.ns - ksel);
+  };
+  int kp[kPerT];
+#pragma unroll
+  for (int u = 0; u < kPerT; ++u) kp[u] = -1;
+  if (direct) {
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u) {
+      const int rr = lo + tid + u * NT;
+      if (rr < hi) kp[u] = known_pos(rr);
+    }
+  } else {
+    for (int rr = lo + tid; rr < hi; rr += NT) {
+      const int p = known_pos(rr);
+      if (p >= 0) frows[rr] = p;
+    }
+  }
   if (r > 0 && cached)
     for (int i = tid; i < n_tie; i += NT) tcache[i] = ld_dev(&ftie[tie_slot(i)]);
   // cluster and weights of the block's own tie i (a head-wide tie index)
@@ -810,26 +853,6 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) atomicAdd(&wsel[(cl - c0) * G + g], to_fixed(w[g]));
   };
-  // this block's rows of the head's exact list [sink | above | tie winners |
-  // recent]: every row but the winners is known already
-  const int n_rec = si.T - si.recent_beg;
-  const int R = si.ns + ksel + n_rec;
-  const int lo = (int)((long long)sub * R / P), hi = (int)((long long)(sub + 1) * R / P);
-  for (int rr = lo + tid; rr < hi; rr += NT) {
-    int p;
-    if (rr < si.ns) {
-      p = rr;
-    } else if (rr < si.ns + n_above) {
-      const int s = rr - si.ns;
-      const int j = seg_of(S.apre, P, s);
-      p = ld_dev(&fpos[S.tbase[j] + (s - S.apre[j])]);
-    } else if (rr < si.ns + ksel) {
-      continue;
-    } else {
-      p = si.recent_beg + (rr - si.ns - ksel);
-    }
-    frows[rr] = p;
-  }
   lds_sync();
   // the r winners of the bucket: the composites >= the r-th largest
   // (prefix under mask)
@@ -909,7 +932,10 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       const unsigned long long rec = tcache[i];
       if (!is_winner(rec)) continue;
       const int row = si.ns + n_above + wi++;
-      if (row >= lo && row < hi) frows[row] = (int32_t)(uint32_t)rec;
+      if (row >= lo && row < hi) {
+        if (direct) posd[row - lo] = (int32_t)(uint32_t)rec;
+        else frows[row] = (int32_t)(uint32_t)rec;
+      }
       if (i >= own0 && i < S.tpre[sub + 1]) own_add(i);
     }
   } else if (r > 0) {
@@ -926,7 +952,10 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       block_scan2<NT>(win, 0, &ow, &dummy, &tw, &td, S.sh);
       if (win) {
         const int row = si.ns + n_above + run + ow;
-        if (row >= lo && row < hi) frows[row] = (int32_t)(uint32_t)rec;
+        if (row >= lo && row < hi) {
+          if (direct) posd[row - lo] = (int32_t)(uint32_t)rec;
+          else frows[row] = (int32_t)(uint32_t)rec;
+        }
         if (i >= own0 && i < S.tpre[sub + 1]) own_add(i);
       }
       run += tw;
@@ -936,7 +965,6 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   // background logits of the block's clusters: log2 of the unselected weight
   // (relative to the cluster max) plus the max
   float* sbg = reinterpret_cast<float*>(hist);
-  long long* ioff = reinterpret_cast<long long*>(dyn + C::kUBytes + 4096);
   for (int i = tid; i < ncl * G; i += NT) {
     const int cl = c0 + i / G, g = i % G;
     const float M = binl[((cl - c0) * G + g) * 2];
@@ -954,12 +982,13 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   // on them are exact.
   RowTileState st;
   tile_init(st);
-  const int nr = hi - lo;
   const int nbg = d.exact_only ? 0 : ncl;
   const int nbt = (nbg + 15) / 16;
   const int32_t* tab = a.table + (size_t)b * d.max_pages;
   const float* means = a.ix.means + ((size_t)bh * d.L + c0) * kD;
-  constexpr int kStage = (int)((C::kHBytes - 4096) / sizeof(long long));
+  // staged offsets: at the top of the LUT region on the direct path, else
+  // after the background logits in the histogram region
+  long long* ioff = direct ? ioffd : reinterpret_cast<long long*>(dyn + C::kUBytes + 4096);
   const int n_ph = max(1, (nr + kStage - 1) / kStage);
   for (int phi = 0; phi < n_ph; ++phi) {
     const int ph = phi * kStage;
@@ -967,12 +996,13 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     __syncthreads();
     {
       // a thread's rows, then their pages, each round of loads issued at once
-      constexpr int kPerT = (kStage + NT - 1) / NT;
       int pr[kPerT], pg[kPerT];
 #pragma unroll
       for (int i = 0; i < kPerT; ++i) {
         const int t = tid + i * NT;
-        pr[i] = t < n ? min(max(frows[lo + ph + t], 0), d.cap - 1) : -1;
+        int p = -1;
+        if (t < n) p = direct ? (kp[i] >= 0 ? kp[i] : posd[t]) : frows[lo + ph + t];
+        pr[i] = t < n ? min(max(p, 0), d.cap - 1) : -1;
       }
 #pragma unroll
       for (int i = 0; i < kPerT; ++i) pg[i] = pr[i] >= 0 ? tab[pr[i] >> 4] : 0;
