@@ -11,7 +11,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["pqhsa_api.hip", "pqhsa_upload.hip", "pqhsa_step.hip", "pqhsa_attn.hip",
+SOURCES = ["pqhsa_host.cpp", "pqhsa_api.hip", "pqhsa_upload.hip", "pqhsa_step.hip", "pqhsa_attn.hip",
            "pqhsa_fused.hip", "pqhsa_append.hip", "pqhsa_reuse.hip"]
 LIB_NAME = "libpqhsa.so"
 ARCH = "gfx950"
@@ -33,7 +33,8 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into ivf_pq_sparse_amd/libpqhsa.so; return its path."""
+    """Compile every source (the HIP kernels and the host logic) into
+    ivf_pq_sparse_amd/libpqhsa.so; return its path."""
     out = os.path.join(HERE, LIB_NAME)
     tmp = out + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(ROOT, "include"),
