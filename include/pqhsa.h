@@ -279,13 +279,20 @@ enum {
   PQHSA_VARIANT_DEFAULT = 0,  /* exactly what pqhsa_decode_step runs */
   PQHSA_VARIANT_STAGED = 1,   /* the six staged kernels, whatever the shape */
   PQHSA_VARIANT_DENSE = 2,    /* pqhsa_dense_decode_step (index_buf unused) */
-  PQHSA_VARIANT_BARRIER_TEST = 3  /* test only: the fused step with barriers that
+  PQHSA_VARIANT_BARRIER_TEST = 3, /* test only: the fused step with barriers that
                                      wait for one block more than there are and
                                      give up after 20 us, so that every wait runs
                                      out (every kernel still ends normally): all
                                      outputs NaN, flags bit 0 set.  Returns
                                      PQHSA_ERR_UNSUPPORTED where the fused step
                                      cannot run the shape. */
+  PQHSA_VARIANT_KEYS_OUT = 4      /* test only: the fused step, which then also
+                                     writes every entry's 16-bit key code into
+                                     the workspace's keys region (by default it
+                                     passes them from its scan to its selection
+                                     in LDS where a block's entries fit).
+                                     Returns PQHSA_ERR_UNSUPPORTED where the
+                                     fused step cannot run the shape. */
 };
 
 /* A decode step that also times its kernels.  events holds 2 * PQHSA_NUM_STAGES
@@ -317,12 +324,13 @@ pqhsa_status pqhsa_decode_step_profiled(const pqhsa_shape* shape, const void* in
  *   flags   uint32: bit 0 set if a barrier wait of the fused step ever timed
  *           out (its results are then not valid)
  * The staged step fills lut, qc, keys, bins, rows, n_rows and partials; the
- * fused step fills qc and bins of every cluster, n_rows, rows in a per-block
- * order, and at the start
- * of keys a 16-bit code of each key as uint16 [B*Hkv][max_context]: the
- * order key's sign, its binary exponent clamped to the 16 binades of
- * [2^-7, 2^9) (the same field range in both halves), then 11 mantissa bits,
- * at least 1 (0 for non-candidates). */
+ * fused step fills qc and bins of every cluster and n_rows; rows only for
+ * blocks whose share of the exact rows exceeds one LDS staging (in a
+ * per-block order); and, under PQHSA_VARIANT_KEYS_OUT or for blocks whose
+ * entries exceed their LDS key cache, at the start of keys a 16-bit code of
+ * each key as uint16 [B*Hkv][max_context]: the order key's sign, its binary
+ * exponent clamped to the 16 binades of [2^-7, 2^9) (the same field range in
+ * both halves), then 11 mantissa bits, at least 1 (0 for non-candidates). */
 /* Also: hist (uint32 [B*Hkv][4096] key histogram, hist_bytes long) and
  * counters (the fused step's per-head barrier counters and flags, the flags
  * word and per-block counts, counters_bytes long): the regions a step expects

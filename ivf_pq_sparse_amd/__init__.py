@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     VARIANT_BARRIER_TEST,
     VARIANT_DEFAULT,
     VARIANT_DENSE,
+    VARIANT_KEYS_OUT,
     VARIANT_STAGED,
     STAGE_NAMES,
     HipEvent,
@@ -93,9 +94,10 @@ class PQHSADecoder:
         self._append_ws = ws          # keep alive until the stream has used it
 
     def step(self, q, k_cache, v_cache, block_table, context_lens, out=None, selected=False,
-             lse=False, stream=None, staged=False):
+             lse=False, stream=None, staged=False, variant=None):
         """One decode step.  staged=True runs the six staged kernels instead
-        of whatever pqhsa_decode_step would choose (for cross-checks)."""
+        of whatever pqhsa_decode_step would choose (for cross-checks);
+        variant runs that variant of pqhsa_decode_step_profiled instead."""
         s = self.shape
         if out is None:
             out = torch.empty(s.batch, s.num_q_heads, 128, dtype=torch.float32, device=self.device)
@@ -103,11 +105,12 @@ class PQHSADecoder:
         sel = (torch.full((s.batch, s.num_kv_heads, max(self.max_selected, 1)), -1,
                           dtype=torch.int32, device=self.device) if selected else None)
         ls = torch.empty(s.batch, s.num_q_heads, dtype=torch.float32, device=self.device) if lse else None
-        if staged:
+        if staged or variant is not None:
             if self._events is None:
                 self._events = [HipEvent() for _ in range(2 * NUM_STAGES)]
             decode_step_profiled(s, self.index, q, k_cache, v_cache, block_table, context_lens,
-                                 out, self.workspace, self._events, variant=VARIANT_STAGED,
+                                 out, self.workspace, self._events,
+                                 variant=VARIANT_STAGED if staged else variant,
                                  selected=sel, lse=ls, stream=stream)
         else:
             decode_step(s, self.index, q, k_cache, v_cache, block_table, context_lens, out,

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libpqhsa.so")
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "buffer too small",
           4: "HIP error"}
 NUM_STAGES = 6
-VARIANT_DEFAULT, VARIANT_STAGED, VARIANT_DENSE, VARIANT_BARRIER_TEST = 0, 1, 2, 3
+VARIANT_DEFAULT, VARIANT_STAGED, VARIANT_DENSE, VARIANT_BARRIER_TEST, VARIANT_KEYS_OUT = 0, 1, 2, 3, 4
 STAGE_NAMES = ["tables", "scan", "collect", "select", "attend", "merge"]
 
 

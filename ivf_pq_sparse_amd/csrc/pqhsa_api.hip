@@ -98,8 +98,8 @@ pqhsa_status run_step(const pqhsa_shape* shape, const void* index_buf, const uin
                       const uint16_t* k_cache, const uint16_t* v_cache,
                       const int32_t* block_table, const int32_t* context_lens, float* out,
                       int32_t* selected, float* lse, void* workspace, size_t ws_bytes,
-                      bool staged, bool barrier_test, hipEvent_t* evs, int* n_kernels,
-                      hipStream_t stream) {
+                      bool staged, bool barrier_test, bool keys_out, hipEvent_t* evs,
+                      int* n_kernels, hipStream_t stream) {
   PQHSA_TRY(validate(shape, false));
   if (!index_buf || !q || !k_cache || !v_cache || !block_table || !context_lens || !out ||
       !workspace)
@@ -114,11 +114,12 @@ pqhsa_status run_step(const pqhsa_shape* shape, const void* index_buf, const uin
   a.q = q; a.kc = k_cache; a.vc = v_cache; a.table = block_table; a.ctx = context_lens;
   a.out = out; a.selected = selected; a.max_sel = max_selected(shape); a.lse = lse;
   const int fP = staged ? 0 : fused_blocks_per_head(d);
-  if (barrier_test && fP == 0) return PQHSA_ERR_UNSUPPORTED;
+  if ((barrier_test || keys_out) && fP == 0) return PQHSA_ERR_UNSUPPORTED;
   if (fP > 0) {
     // the whole step in one kernel
     a.d.fP = fP;
     a.d.fcpb = ceil_div(d.L, fP);
+    a.d.fkeys_out = keys_out ? 1 : 0;
     if (barrier_test) {
       // one arrival more than there are blocks: every barrier wait runs out
       a.d.fbar_extra = 1;
@@ -338,8 +339,8 @@ pqhsa_status pqhsa_decode_step(const pqhsa_shape* shape, const void* index_buf,
                                float* lse, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
   return run_step(shape, index_buf, q, k_cache, v_cache, block_table, context_lens, out,
-                  selected, lse, workspace, workspace_bytes, false, false, nullptr, nullptr,
-                  stream);
+                  selected, lse, workspace, workspace_bytes, false, false, false, nullptr,
+                  nullptr, stream);
 }
 
 pqhsa_status pqhsa_decode_step_noalloc(const pqhsa_shape* shape, const void* index_buf,
@@ -367,7 +368,8 @@ pqhsa_status pqhsa_decode_step_noalloc(const pqhsa_shape* shape, const void* ind
                      reinterpret_cast<uint4*>(ws + l.fsync), ctr_bytes / 16);
   PQHSA_TRY(hip_status(hipGetLastError()));
   return run_step(shape, index_buf, q, k_cache, v_cache, block_table, context_lens, out,
-                  selected, lse, ws, kScratchBytes, false, false, nullptr, nullptr, stream);
+                  selected, lse, ws, kScratchBytes, false, false, false, nullptr, nullptr,
+                  stream);
 }
 
 pqhsa_status pqhsa_dense_decode_step(const pqhsa_shape* shape, const uint16_t* q,
@@ -394,9 +396,11 @@ pqhsa_status pqhsa_decode_step_profiled(const pqhsa_shape* shape, const void* in
     case PQHSA_VARIANT_DEFAULT:
     case PQHSA_VARIANT_STAGED:
     case PQHSA_VARIANT_BARRIER_TEST:
+    case PQHSA_VARIANT_KEYS_OUT:
       st = run_step(shape, index_buf, q, k_cache, v_cache, block_table, context_lens, out,
                     selected, lse, workspace, workspace_bytes, variant == PQHSA_VARIANT_STAGED,
-                    variant == PQHSA_VARIANT_BARRIER_TEST, events, &nk, stream);
+                    variant == PQHSA_VARIANT_BARRIER_TEST, variant == PQHSA_VARIANT_KEYS_OUT,
+                    events, &nk, stream);
       break;
     case PQHSA_VARIANT_DENSE:
       st = run_dense(shape, q, k_cache, v_cache, block_table, context_lens, out, lse, workspace,

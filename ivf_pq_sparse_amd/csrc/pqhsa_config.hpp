@@ -62,6 +62,8 @@ struct Dims {
   int fbar_extra;             // fused step: arrivals a barrier waits for beyond its P blocks
                               //   (0; 1 only in the barrier test, so that every wait runs out)
   unsigned int fbar_ticks;    // fused step: bound of a barrier wait in ticks of the 100 MHz clock
+  int fkeys_out;              // fused step: also write the 16-bit keys to the workspace
+                              //   (always done where a block's keys exceed its LDS key cache)
 };
 
 constexpr unsigned int kBarrierTicks = 200000000u;   // 2 s: the fused step's default wait bound

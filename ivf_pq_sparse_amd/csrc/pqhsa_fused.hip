@@ -68,7 +68,11 @@ struct FusedCfg {
   static constexpr size_t kWBytes = (size_t)kCG * sizeof(unsigned long long);   // selected weights
   static constexpr size_t kQBytes = (size_t)kCG * sizeof(float);                // cluster logits
   static constexpr size_t kBBytes = (size_t)kCG * 2 * sizeof(float);            // cluster (max, sum)
-  static constexpr size_t kDyn = kUBytes + kHBytes + kWBytes + kQBytes + kBBytes;
+  // 16-bit keys of the block's entries, from the scan to phase 2, when the
+  // block has at most kKeyCap entries (none at G = 8: no LDS left)
+  static constexpr int kKeyCap = G == 8 ? 0 : 8192;
+  static constexpr size_t kKBytes = (size_t)kKeyCap * sizeof(uint16_t);
+  static constexpr size_t kDyn = kUBytes + kHBytes + kWBytes + kQBytes + kBBytes + kKBytes;
   static constexpr int kTieCap = (int)(kUBytes / sizeof(unsigned long long));
 };
 
@@ -292,6 +296,11 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   const int32_t* off = a.ix.list_off + (size_t)bh * (d.L + 1);
   auto entry_at = [&](int c) { return min(max(off[c], 0), d.cap); };
   const int E0 = entry_at(c0), E1 = max(E0, entry_at(c1));
+  // the scan's keys reach phase 2 through LDS when they fit, else through
+  // the workspace (which also gets them when asked to)
+  uint16_t* klds = reinterpret_cast<uint16_t*>(dyn + C::kDyn - C::kKBytes);
+  const bool lkeys = E1 - E0 <= C::kKeyCap;
+  const bool gkeys = !lkeys || d.fkeys_out != 0;
   const SeqInfo si = seq_info(d, a.ctx, a.ix.n_indexed, b);
   // the head's three counters (barrier 1, barrier 2, finished blocks), each on
   // its own cache line: heads and counters do not contend for one line
@@ -514,7 +523,8 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
 #pragma unroll
           for (int g = 0; g < G; ++g) s[t][g] = v[g];
         }
-        keys[e] = (uint16_t)code;
+        if (lkeys) klds[e - E0] = (uint16_t)code;
+        if (gkeys) keys[e] = (uint16_t)code;
       }
     }
 #pragma unroll
@@ -583,7 +593,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int e = E0 + u * NT + tid;
-    pk[u] = e < E1 ? keys[e] : 0u;
+    pk[u] = e < E1 ? (lkeys ? klds[e - E0] : keys[e]) : 0u;
   }
   barrier_wait(&sync[0], nbar, a.ws.fflags, hflag, d.fbar_ticks, last1);
 
@@ -702,7 +712,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
           const int e = cb + kChunk + u * NT + tid;
-          pk[u] = e < E1 ? keys[e] : 0u;
+          pk[u] = e < E1 ? (lkeys ? klds[e - E0] : keys[e]) : 0u;
         }
       }
       int oa, ot, ta, tt;

@@ -40,11 +40,12 @@ def poison_workspace(dec):
 
 
 def run_gpu(inp, dense=False, want_selected=True, page_seed=0, spare_pages=0, max_context=None,
-            staged=False, background=True, poison=False):
+            staged=False, background=True, poison=False, variant=None):
     """Stage `inp`, upload the index and run one step; return numpy results.
     staged=True runs the six staged kernels instead of the default path;
     background=False sets exact_only (no background term); poison=True fills
-    the workspace's scratch with NaN bytes first."""
+    the workspace's scratch with NaN bytes first; variant runs that variant
+    of the profiled entry point."""
     tens, kw = stage(inp, "cuda", page_seed=page_seed, spare_pages=spare_pages,
                      max_context=max_context)
     shape = pq.make_shape(**kw, exact_only=0 if background else 1)
@@ -60,7 +61,8 @@ def run_gpu(inp, dense=False, want_selected=True, page_seed=0, spare_pages=0, ma
     dec.upload(tens["centroids"], tens["codebooks"], tens["list_ids"], tens["codes"],
                tens["n_indexed"], tens["v_cache"], tens["block_table"])
     out, sel, lse = dec.step(tens["q"], tens["k_cache"], tens["v_cache"], tens["block_table"],
-                             tens["context_lens"], selected=want_selected, lse=True, staged=staged)
+                             tens["context_lens"], selected=want_selected, lse=True, staged=staged,
+                             variant=variant)
     torch.cuda.synchronize()
     assert dec.flags() == 0, "a barrier wait of the fused step timed out"
     res = dict(O=out.cpu().numpy().astype(np.float64), lse=lse.cpu().numpy(), shape=shape,

@@ -218,7 +218,9 @@ def test_tables_and_keys_match_oracle(staged):
     from oracle import pqhsa_oracle as orc
     inp = make_step_inputs(1, context_lens=[4000], num_q_heads=8, num_kv_heads=2, num_lists=24,
                            workload_id=31)
-    g = run_gpu(inp, staged=staged)
+    # the fused step passes its keys to its selection in LDS; the keys-out
+    # variant also writes them to the workspace
+    g = run_gpu(inp, staged=staged, variant=None if staged else pq.VARIANT_KEYS_OUT)
     shape, dec = g["shape"], g["dec"]
     lay = pq.workspace_layout(shape)
     ws = dec.workspace
