@@ -63,6 +63,8 @@ def parse():
                    help="print a markdown table of a sweep instead of the JSON line")
     p.add_argument("--summarize-profile", nargs=4, metavar=("TRACE", "FETCH", "WRITE", "OUT"),
                    help="write the markdown summary of three rocprofv3 output folders and exit")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "OUT"),
+                   help="write the markdown table of one rocprofv3 --pmc run and exit")
     p.add_argument("--profile-command", default="",
                    help="the command line recorded in the summary")
     return p.parse_args()
@@ -205,6 +207,34 @@ def summarize_profile(trace_dir, fetch_dir, write_dir, out, command):
             lines.append(f"{k} {float(r['AverageNs']):.0f} {b:.0f}")
     lines += ["```", ""]
     open(out, "w").write("\n".join(lines))
+    print(f"wrote {out}", file=sys.stderr)
+
+
+def summarize_counters(counter_dir, out, command, kernels):
+    """Markdown table of the mean value per dispatch of every counter of one
+    rocprofv3 --pmc run, for the named kernels (prefix match)."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(counter_dir, "*counter_collection.csv"))
+    if not f:
+        raise SystemExit(f"no counter_collection.csv under {counter_dir}")
+    acc = {}
+    for r in csv.DictReader(open(f[0])):
+        k = _short_kernel(r["Kernel_Name"])
+        if not any(k.startswith(x) for x in kernels):
+            continue
+        acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    names = sorted({c for v in acc.values() for c in v})
+    lines = ["# rocprofv3 counters per dispatch (mean over dispatches)", "",
+             "Command (run from the repository root):", "", "```", command, "```", "",
+             f"source_sha256: {source_digest()}", "",
+             "| kernel | dispatches | " + " | ".join(names) + " |",
+             "|---|---|" + "---|" * len(names)]
+    for k in sorted(acc):
+        n = max(len(v) for v in acc[k].values())
+        lines.append(f"| {k} | {n} | " + " | ".join(
+            f"{np.mean(acc[k][c]):.4g}" if c in acc[k] else "" for c in names) + " |")
+    open(out, "w").write("\n".join(lines) + "\n")
     print(f"wrote {out}", file=sys.stderr)
 
 
@@ -557,6 +587,10 @@ def main():
     args = parse()
     if args.summarize_profile:
         summarize_profile(*args.summarize_profile, command=args.profile_command)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, command=args.profile_command,
+                           kernels=("k_fused", "k_dense_mfma", "k_attend", "k_scan", "k_merge"))
         return
     if args.sweep:
         sweep(args.sweep, args.steps, args.warmup)
