@@ -129,7 +129,7 @@ def source_digest():
     h = hashlib.sha256()
     d = os.path.join(ROOT, "ivf_pq_sparse_amd", "csrc")
     for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".hpp", ".h")):
+        if f.endswith((".hip", ".hpp", ".h", ".cpp")):
             h.update(f.encode())
             h.update(open(os.path.join(d, f), "rb").read())
     h.update(open(os.path.join(ROOT, "include", "pqhsa.h"), "rb").read())
