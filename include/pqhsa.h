@@ -249,7 +249,8 @@ pqhsa_status pqhsa_decode_step_noalloc(const pqhsa_shape* shape, const void* ind
 
 /*
  * Dense split-K decode attention over each sequence's whole context, through
- * the same exact-attention and merge kernels as pqhsa_decode_step.  This is
+ * the same exact-attention row tiles (16-row MFMA tiles, online softmax) as
+ * pqhsa_decode_step, and the staged step's log-sum-exp merge kernel.  This is
  * the honest baseline: the activation/KV-sparsity crossover article
  * (rit.work blog, section "Why one method gives different speed-ups") runs
  * dense and sparse modes through one split-K kernel, because a slower dense
