@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="layer copies (0 = enough to exceed MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the graph-replayed timing (profiled runs)")
     p.add_argument("--no-other-workloads", action="store_true",
                    help="skip the 32K, 16 x 128K and 512K lines beside the main workload")
     p.add_argument("--copy-calibration", action="store_true",
@@ -682,6 +684,33 @@ def main():
         marks[-1].synchronize()
         return [marks[i].elapsed_ms(marks[i + 1]) * 1e3 for i in range(n)]
 
+    def graph_us(dense):
+        """µs per step when `steps` steps are captured once in a HIP graph
+        (torch.cuda.graph) and the graph is replayed: the host launch work
+        the eager loop pays per step is paid once per replay.  The steps
+        clear their own counters in their kernels, so a replay is exact."""
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for i in range(args.warmup):
+                step(i, dense)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(i, dense)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = pq.HipEvent(), pq.HipEvent()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        e1.synchronize()
+        torch.cuda.synchronize()
+        del graph
+        return e0.elapsed_ms(e1) / args.steps * 1e3
+
     def spread(per):
         if not per:
             return None
@@ -696,6 +725,11 @@ def main():
     dense_reps = [] if args.no_dense else per_step(True)
     if dense_ms is not None:
         log(f"dense split-K step: {dense_ms * 1e3:.2f} µs")
+    graph_step = None if args.no_graph else graph_us(False)
+    graph_dense = None if args.no_graph or args.no_dense else graph_us(True)
+    if graph_step is not None:
+        log(f"graph-replayed steps: PQ-HSA {graph_step:.2f} µs"
+            + (f", dense {graph_dense:.2f} µs" if graph_dense is not None else ""))
 
     # per-kernel durations: the same steps through the profiled entry point,
     # every kernel with its own start/stop events on the step's stream
@@ -819,6 +853,9 @@ def main():
         "step_us_spread": spread(step_reps),
         "dense_us": dense_ms * 1e3 if dense_ms else None,
         "dense_us_spread": spread(dense_reps),
+        "graph_replay_us": ({"step": graph_step, "dense": graph_dense,
+                             "source": f"{args.steps} steps captured in one HIP graph, "
+                                       "one timed replay"} if graph_step is not None else None),
         "speedup_vs_dense": (dense_ms / ms) if dense_ms else None,
         "step_alg_bytes": step_bytes,
         "step_alg_gbps": step_bytes / (ms * 1e-3) / 1e9,
