@@ -256,12 +256,14 @@ def stored_traffic(path):
     return out
 
 
-def kernel_of_stage(stage, G):
-    """Kernel symbol (as rocprofv3 shortens it) that a stage launches."""
+def kernel_of_stage(stage, G, n_parts=0):
+    """Kernel symbol (as rocprofv3 shortens it) that a stage launches (the
+    merge kernel's template argument is its number of part groups)."""
+    ng = 2 if n_parts <= 64 else 4 if n_parts <= 128 else 8
     return {"fused": f"k_fused<{G}>",
             "tables": f"k_tables<{G}>", "scan": f"k_scan<{G}>", "collect": f"k_collect<{G}>",
             "select": f"k_select<{G}>", "attend": f"k_attend<{G},0>",
-            "merge": "k_merge"}[stage]
+            "merge": f"k_merge<{ng}>"}[stage]
 
 
 class Rig:
@@ -787,7 +789,7 @@ def main():
     achieved = dom_bytes / (stage_us[dom] * 1e-6) / 1e9
     prof = stored_traffic(os.path.join(ROOT, "profiles", f"counters_{w['name']}.md"))
     G = shape.num_q_heads // shape.num_kv_heads
-    kname = kernel_of_stage(names[dom], G)
+    kname = kernel_of_stage(names[dom], G, lay.n_parts)
     traffic = prof[kname][1] if prof and kname in prof else None
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

@@ -422,12 +422,15 @@ __global__ __launch_bounds__(256) void k_attend(StepArgs a) {
 }
 
 // Log-sum-exp merge of one query head's n_parts partials into O and the
-// log-sum-exp.  grid (B*Hq), 256 threads = 2 halves of the parts x 128 dims.
-// The parts' maxima and sums are staged in LDS; each thread then sums its dim
-// over its half of the parts, issuing 16 loads before using any.
-__global__ __launch_bounds__(256) void k_merge(StepArgs a) {
-  extern __shared__ float mlds[];   // [np] weights, [np] sums, [128] second half's sums
-  __shared__ float red[8];
+// log-sum-exp.  grid (B*Hq), 128 x NG threads = NG groups of the parts (2, 4
+// or 8, more for more parts) x 128 dims.  The parts' maxima and sums are
+// staged in LDS; each thread then sums its dim over its group's parts,
+// issuing 16 loads before using any, and the groups' sums add pairwise.
+template <int NG>
+__global__ __launch_bounds__(128 * NG) void k_merge(StepArgs a) {
+  constexpr int NW = 2 * NG;
+  extern __shared__ float mlds[];   // [np] weights, [np] sums, [NG][128] the groups' sums
+  __shared__ float red[2 * NW];
   const int G = a.d.G;
   int bh, g;
   xcd_map(blockIdx.x, a.d.B * a.d.Hkv, G, &bh, &g);
@@ -438,7 +441,7 @@ __global__ __launch_bounds__(256) void k_merge(StepArgs a) {
   const float* part = a.ws.partials + (size_t)bq * a.d.n_parts * kPart;
   float* wts = mlds;
   float* ls = mlds + np;
-  float* half1 = mlds + 2 * np;
+  float* gsum = mlds + 2 * np;
   float mx = -INFINITY;
   for (int i = tid; i < np; i += blockDim.x) {
     const float m = part[(size_t)i * kPart];
@@ -449,7 +452,9 @@ __global__ __launch_bounds__(256) void k_merge(StepArgs a) {
   mx = wave_max(mx);
   if (lane == 0) red[wave] = mx;
   __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float M = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, red[w]);
   float lsum = 0.0f;
   for (int i = tid; i < np; i += blockDim.x) {
     const float m = wts[i];
@@ -459,12 +464,20 @@ __global__ __launch_bounds__(256) void k_merge(StepArgs a) {
   }
   lsum = wave_sum(lsum);
   __syncthreads();
-  if (lane == 0) red[4 + wave] = lsum;
+  if (lane == 0) red[NW + wave] = lsum;
   __syncthreads();
-  const float L = (red[4] + red[5]) + (red[6] + red[7]);
-  const int dim = tid & (kD - 1), half = tid >> 7;
-  const int hp = (np + 1) / 2;
-  const int i0 = half * hp, i1 = min(np, i0 + hp);
+  // pairwise over the waves, neighbours first
+  float t[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) t[w] = red[NW + w];
+#pragma unroll
+  for (int n = NW; n > 1; n >>= 1)
+#pragma unroll
+    for (int w = 0; w < n / 2; ++w) t[w] = t[2 * w] + t[2 * w + 1];
+  const float L = t[0];
+  const int dim = tid & (kD - 1), grp = tid >> 7;
+  const int hp = (np + NG - 1) / NG;
+  const int i0 = grp * hp, i1 = min(np, i0 + hp);
   const float* pd = part + 4 + dim;
   float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int i = i0; i < i1; i += 16) {
@@ -475,11 +488,14 @@ __global__ __launch_bounds__(256) void k_merge(StepArgs a) {
     for (int u = 0; u < 16; ++u)
       if (i + u < i1) A[u & 3] = fmaf(wts[i + u], x[u], A[u & 3]);
   }
-  const float sum = (A[0] + A[1]) + (A[2] + A[3]);
-  if (half == 1) half1[dim] = sum;
+  gsum[grp * kD + dim] = (A[0] + A[1]) + (A[2] + A[3]);
   __syncthreads();
-  if (half == 0) {
-    const float tot = sum + half1[dim];
+  if (grp == 0) {
+#pragma unroll
+    for (int n = NG; n > 1; n >>= 1)
+#pragma unroll
+      for (int k = 0; k < n / 2; ++k) gsum[k * kD + dim] += gsum[(k + n / 2) * kD + dim];
+    const float tot = gsum[dim];
     // no rows at all: O = 0, lse = -inf; a NaN sum stays NaN (never hidden)
     a.out[(size_t)bq * kD + dim] = L != 0.0f ? tot / L : 0.0f;
     if (dim == 0 && a.lse) a.lse[bq] = L != 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
@@ -539,11 +555,14 @@ hipError_t launch_exact_reuse(const StepArgs& a, const Launch& l) {
 }
 
 hipError_t launch_merge(const StepArgs& a, const Launch& l) {
-  const size_t lds = ((size_t)2 * a.d.n_parts + kD) * sizeof(float);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_merge),
+  // groups of the parts: at most 32 parts per thread
+  const int ng = a.d.n_parts <= 64 ? 2 : a.d.n_parts <= 128 ? 4 : 8;
+  const size_t lds = ((size_t)2 * a.d.n_parts + (size_t)ng * kD) * sizeof(float);
+  auto kern = ng == 2 ? k_merge<2> : ng == 4 ? k_merge<4> : k_merge<8>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  return launch_kernel(k_merge, dim3(a.d.B * a.d.Hq), dim3(256), lds, l, a);
+  return launch_kernel(kern, dim3(a.d.B * a.d.Hq), dim3(kD * ng), lds, l, a);
 }
 
 }  // namespace pqhsa
