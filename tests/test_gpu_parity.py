@@ -23,7 +23,8 @@ from pqhsa_synth import make_step_inputs  # noqa: E402
 
 # ------------------------------------------------------------------ dense baseline
 @pytest.mark.parametrize("T,G,Hkv", [(8192, 4, 1), (1000, 4, 2), (37, 8, 1), (5000, 1, 3),
-                                     (2049, 2, 2), (3000, 2, 8), (4100, 4, 4), (700, 1, 6)])
+                                     (2049, 2, 2), (3000, 2, 8), (4100, 4, 4), (700, 1, 6),
+                                     (20000, 2, 1)])
 def test_dense_matches_oracle(T, G, Hkv):
     import oracle
     inp = make_step_inputs(0, context_lens=[T], num_q_heads=G * Hkv, num_kv_heads=Hkv,
