@@ -588,7 +588,11 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   }
   const bool last1 = barrier_arrive(&sync[0], nbar);
   // while waiting: this block's first keys for the classification below
-  constexpr int kPer = 16;
+  // (kPer per thread, so that phase 2 takes a block's entries in one chunk
+  // when it holds up to NT * kPer of them: 18 at G = 8, whose blocks at the
+  // 512K shape hold 7.9K-8.4K entries; 16 elsewhere, where 18 measured
+  // slower at the 16-sequence batch)
+  constexpr int kPer = G == 8 ? 18 : 16;
   uint32_t pk[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {

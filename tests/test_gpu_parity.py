@@ -367,17 +367,19 @@ def test_full_budget_long_context_few_clusters():
     parity(inp, what="budget 100 % at 64K, 8 clusters")
 
 
+@pytest.mark.parametrize("G", [4, 8])
 @pytest.mark.parametrize("budget_bp", [2500, 6000])
-def test_many_key_chunks_per_block(budget_bp):
+def test_many_key_chunks_per_block(budget_bp, G):
     # 2 clusters over 64K tokens: 2 blocks of 32K entries, four key chunks
-    # each.  At 25 % some chunks' chosen entries fit the block's list and
-    # others are recorded directly, so a listed chunk must be recorded before
-    # a later chunk is recorded at the slots after it; at 60 % every chunk
-    # chooses more than the list holds and records its own entries
+    # each (8192 entries per chunk at G = 4, 9216 at G = 8).  At 25 % some
+    # chunks' chosen entries fit the block's list and others are recorded
+    # directly, so a listed chunk must be recorded before a later chunk is
+    # recorded at the slots after it; at 60 % every chunk chooses more than
+    # the list holds and records its own entries
     inp = make_step_inputs(0, context_lens=[65536], num_lists=2, budget_bp=budget_bp,
-                           workload_id=18)
-    log(f"[pqhsa] budget {budget_bp} bp at 64K over 2 clusters")
-    parity(inp, what=f"budget {budget_bp} bp at 64K, 2 clusters")
+                           num_q_heads=G, num_kv_heads=1, workload_id=18)
+    log(f"[pqhsa] budget {budget_bp} bp at 64K over 2 clusters, G={G}")
+    parity(inp, what=f"budget {budget_bp} bp at 64K, 2 clusters, G={G}")
 
 
 def _random_case(seed):
