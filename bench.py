@@ -343,7 +343,7 @@ class Rig:
         return e0.elapsed_ms(e1) / steps * 1e3
 
 
-def other_workloads(main_wid, steps=64, warmup=8):
+def other_workloads(main_wid, steps=128, warmup=64):
     """The 32K, 16 x 128K and 512K workloads beside the main one: PQ-HSA and
     dense split-K µs per step on rotated layer copies, the speed-up and the
     step's algorithmic bytes and rate."""
