@@ -52,7 +52,7 @@ WsPtrs ws_ptrs(const Dims& d, bool dense, void* buf) {
     w.fsync = reinterpret_cast<uint32_t*>(p + l.fsync);
     w.fflags = reinterpret_cast<uint32_t*>(p + l.fflags);
     w.fcnt = reinterpret_cast<unsigned long long*>(p + l.fcnt);
-    w.fpart = reinterpret_cast<float*>(p + l.fpart);
+    w.fpart = reinterpret_cast<unsigned long long*>(p + l.fpart);
   }
   w.partials = reinterpret_cast<float*>(p + l.partials);
   return w;

@@ -26,14 +26,17 @@
 //   barrier  (counts and records complete)
 //   phase 3  every block resolves the tie bucket alike (64-bit composite:
 //            the full key, then the inverted position, so equal keys prefer
-//            the lower position; rank counting for a few ties, a radix select
-//            for many), takes an even share of the exact rows (sink, selected,
-//            recent/tail) plus its own clusters' background terms, attends
-//            them in the 16-row MFMA tiles of the dense step, and writes one
-//            partial (m, l, acc[128]) per query head.  The last block of the head to finish merges the P
-//            partials into O and the log-sum-exp, writes the ascending selected
-//            positions if asked, and clears the head's counters and histogram
-//            for the next step.
+//            the lower position; rank counting for up to 512 ties, 128 at
+//            G = 8, else a radix select), takes an even share of the exact
+//            rows (sink, selected, recent/tail) plus its own clusters'
+//            background terms, attends them in the 16-row MFMA tiles of the
+//            dense step, and writes one partial (m, l, acc[128]) per query
+//            head.  The P partials are merged into O and the log-sum-exp by
+//            the head's last block to finish (found by a counter), or at
+//            G = 8 by one merger block per query head that polls tagged
+//            partials; the last block (block 0 at G = 8) writes the
+//            ascending selected positions if asked and clears the head's
+//            counters and histogram for the next step.
 //
 // Cross-block data moves only through device-scope stores, loads and atomics
 // (coherent across XCDs without cache write-back or invalidation); a thread
@@ -76,14 +79,19 @@ struct FusedCfg {
   static constexpr int kTieCap = (int)(kUBytes / sizeof(unsigned long long));
 };
 
-constexpr int kRankMax = 512;   // threshold-bucket ties resolved by counting ranks
+// Threshold-bucket ties resolved by counting ranks, at most: a tie bucket at
+// the 512K shape (G = 8) holds ~200 ties, for which the radix select is faster.
+template <int G>
+constexpr int kRankMax = G == 8 ? 128 : 512;
 
 struct FusedStatic {
   unsigned long long thr;   // the r-th largest tie composite
+  uint32_t dif[2];  // bits at which cached tie composites differ (low, high word)
   int nextc;        // the scan's next unclaimed cluster of the block
   int sh[40];
   uint32_t rh[256];
   int res[4];
+  int tout;         // 1: a barrier wait of this block ran out
   int apre[kMaxFusedP + 1];
   int tpre[kMaxFusedP + 1];
   int tbase[kMaxFusedP + 1];
@@ -127,7 +135,8 @@ __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0xF70); 
 // operations have completed, then one thread adds to the head's counter (true
 // in thread 0 when this block arrived last).  Wait: thread 0 polls until all
 // have arrived or `ticks` of the 100 MHz clock have passed; then bit 0 of
-// *flags and of *hflag (the head's own word) are set.
+// *flags (the workspace's word), of *hflag (the head's) and of *tout (the
+// block's, in LDS) are set.
 __device__ bool barrier_arrive(uint32_t* ctr, uint32_t n) {
   wait_mem();
   __syncthreads();
@@ -138,7 +147,7 @@ __device__ bool barrier_arrive(uint32_t* ctr, uint32_t n) {
 }
 
 __device__ void barrier_wait(uint32_t* ctr, uint32_t n, uint32_t* flags, uint32_t* hflag,
-                             unsigned int ticks, bool last) {
+                             int* tout, unsigned int ticks, bool last) {
   if (threadIdx.x == 0 && !last) {
     const unsigned long long t0 = wall_clock64();
     while (ld_dev(ctr) < n) {
@@ -146,6 +155,7 @@ __device__ void barrier_wait(uint32_t* ctr, uint32_t n, uint32_t* flags, uint32_
       if (wall_clock64() - t0 > ticks) {
         __hip_atomic_fetch_or(flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_fetch_or(hflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *tout = 1;
         break;
       }
     }
@@ -307,6 +317,14 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   uint32_t* sync = a.ws.fsync + (size_t)bh * 3 * kSyncStride;
   // the head's timeout flag shares the finished-blocks line
   uint32_t* hflag = sync + 2 * kSyncStride + 1;
+  // The head's partials, [G][kMaxFusedP][kPart].  At G = 8 (tagged) each word
+  // is 64-bit, a float (low half) and a tag (high half: 0 not written in this
+  // step, 1 written, 2 written by a block one of whose barrier waits ran
+  // out), and mergers poll the tags; elsewhere plain floats that the head's
+  // last block reads after the finished-blocks counter.
+  constexpr bool kTagged = G == 8;
+  unsigned long long* hpart = a.ws.fpart + (size_t)bh * G * kMaxFusedP * kPart;
+  float* hpartf = reinterpret_cast<float*>(a.ws.fpart) + (size_t)bh * G * kMaxFusedP * kPart;
   const uint32_t nbar = (uint32_t)(P + d.fbar_extra);   // arrivals a barrier waits for
   uint32_t* ghist = a.ws.hist + (size_t)bh * kHistBins;
   // the top 16 bits of each entry's selection key (0: not a candidate),
@@ -467,7 +485,10 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     }
     for (int i = tid; i < kHistBins; i += NT) hist[i] = 0u;
     for (int i = tid; i < ncl * G; i += NT) wsel[i] = 0ull;
-    if (tid == 0) S.nextc = c0 + NW;
+    if (tid == 0) {
+      S.nextc = c0 + NW;
+      S.tout = 0;
+    }
   }
   // LDS only: the scan's first round stays in flight
   lds_sync();
@@ -587,6 +608,13 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     }
   }
   const bool last1 = barrier_arrive(&sync[0], nbar);
+  if constexpr (kTagged) {
+    // while waiting: this block's partial slots are marked unwritten; the
+    // stores complete before the block arrives at barrier 2, so no merger
+    // (which reads after barrier 2) can take a slot left from an earlier step
+    for (int i = tid; i < G * kPart; i += NT)
+      st_dev(&hpart[((size_t)(i / kPart) * kMaxFusedP + sub) * kPart + i % kPart], 0ull);
+  }
   // while waiting: this block's first keys for the classification below
   // (kPer per thread, so that phase 2 takes a block's entries in one chunk
   // when it holds up to NT * kPer of them: 18 at G = 8, whose blocks at the
@@ -599,7 +627,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     const int e = E0 + u * NT + tid;
     pk[u] = e < E1 ? (lkeys ? klds[e - E0] : keys[e]) : 0u;
   }
-  barrier_wait(&sync[0], nbar, a.ws.fflags, hflag, d.fbar_ticks, last1);
+  barrier_wait(&sync[0], nbar, a.ws.fflags, hflag, &S.tout, d.fbar_ticks, last1);
 
   // ======================================================= phase 2: threshold bucket
   // the head's histogram from read_lo up: exact there, because every block
@@ -761,7 +789,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) ownw[i * G + g] = ow[g];
   }
-  barrier_wait(&sync[kSyncStride], nbar, a.ws.fflags, hflag, d.fbar_ticks, last2);
+  barrier_wait(&sync[kSyncStride], nbar, a.ws.fflags, hflag, &S.tout, d.fbar_ticks, last2);
 
   // ======================================================= phase 3: ties, rows, partials
   // the queries as the row tiles' B operand, loaded now so that their latency
@@ -848,6 +876,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   }
   if (r > 0 && cached)
     for (int i = tid; i < n_tie; i += NT) tcache[i] = ld_dev(&ftie[tie_slot(i)]);
+  if (G == 8 && tid == 0) { S.dif[0] = 0u; S.dif[1] = 0u; }
   // cluster and weights of the block's own tie i (a head-wide tie index)
   auto own_add = [&](int i) {
     const int t = i - own0;
@@ -872,7 +901,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   // (prefix under mask)
   unsigned long long prefix = 0, mask = 0;
   const bool all = r >= n_tie;
-  if (r > 0 && !all && cached && n_tie <= kRankMax) {
+  if (r > 0 && !all && cached && n_tie <= kRankMax<G>) {
     // few ties: each one counts the ties above it; the one with r - 1 above
     // is the r-th largest (composites are distinct: positions are)
     for (int i = tid; i < n_tie; i += NT) {
@@ -885,9 +914,31 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     prefix = S.thr;
     mask = ~0ull;
   } else if (r > 0 && !all) {
-    // many ties: radix select, 8 bits at a time from the top
+    // many ties: radix select over the composites, 8 bits at a time; at
+    // G = 8 from the highest bit at which the cached ties differ (they share
+    // every bit above it: the bucket's and more), where one round usually
+    // isolates the r-th largest; else from the top
+    int s0 = 56;
+    if (G == 8 && cached) {
+      const unsigned long long c0v = tie_composite(tcache[0]);
+      unsigned long long dv = 0;
+      for (int i = tid; i < n_tie; i += NT) dv |= tie_composite(tcache[i]) ^ c0v;
+      uint32_t lo32 = (uint32_t)dv, hi32 = (uint32_t)(dv >> 32);
+      for (int o = 32; o >= 1; o >>= 1) {
+        lo32 |= __shfl_xor(lo32, o);
+        hi32 |= __shfl_xor(hi32, o);
+      }
+      if (lane == 0 && (lo32 | hi32)) {
+        atomicOr(&S.dif[0], lo32);
+        atomicOr(&S.dif[1], hi32);
+      }
+      lds_sync();
+      const unsigned long long dif = ((unsigned long long)S.dif[1] << 32) | S.dif[0];
+      // dif != 0 when the composites are distinct (positions are)
+      s0 = dif ? max(63 - __clzll((long long)dif) - 7, 0) : 0;
+    }
     int need = r;
-    for (int s = 56;; s -= 8) {
+    for (int s = s0;; s = max(s - 8, 0)) {
       constexpr unsigned long long dm = 0xffull;
       for (int i = tid; i < 256; i += NT) S.rh[i] = 0;
       lds_sync();
@@ -1124,74 +1175,200 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
       L = fmaf(f, mlw[(w * G + g) * 2 + 1], L);
       A = fmaf(f, accw[(w * G + g) * kAS + dim], A);
     }
-    float* out = a.ws.fpart + (((size_t)bh * G + g) * kMaxFusedP + sub) * kPart;
-    st_dev(&out[4 + dim], A);
-    if (dim == 0) {
-      st_dev(&out[0], M);
-      st_dev(&out[1], L);
+    if constexpr (kTagged) {
+      unsigned long long* out = hpart + ((size_t)g * kMaxFusedP + sub) * kPart;
+      const unsigned long long tag = (unsigned long long)(S.tout ? 2u : 1u) << 32;
+      st_dev(&out[4 + dim], tag | __float_as_uint(A));
+      if (dim == 0) {
+        st_dev(&out[0], tag | __float_as_uint(M));
+        st_dev(&out[1], tag | __float_as_uint(L));
+      }
+    } else {
+      float* out = hpartf + ((size_t)g * kMaxFusedP + sub) * kPart;
+      st_dev(&out[4 + dim], A);
+      if (dim == 0) {
+        st_dev(&out[0], M);
+        st_dev(&out[1], L);
+      }
     }
   }
-  wait_mem();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old =
-        __hip_atomic_fetch_add(&sync[2 * kSyncStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    S.last = old == (uint32_t)(P - 1);
-  }
-  __syncthreads();
-  if (!S.last) return;
 
-  // ======================================================= last block of the head
-  // every (head, dim) thread loads its column of the P partials (a wave's
-  // loads of one partial are contiguous) while one wave per head loads the
-  // (m, l) pairs and forms the weights of the partials against the head's max.
-  // A head one of whose barrier waits ran out gets NaN instead: its partials
-  // may be built on an incomplete histogram or incomplete records.
-  const bool timed_out = ld_dev(hflag) != 0u;
-  {
-    float* fp = reinterpret_cast<float*>(hist);     // [G][64] weights
-    float* mlh = fp + G * kMaxFusedP;               // [G][2] head max and sum
-    constexpr int kOut = (G * kD + NT - 1) / NT;    // outputs per thread
-    const float* pbase = a.ws.fpart + (size_t)bh * G * kMaxFusedP * kPart;
-    float x[kMaxFusedP];
-    auto load_col = [&](int o) {
-      // threads past the outputs load a valid column and discard it
-      const int idx = min(tid + o * NT, G * kD - 1);
-      const float* col = pbase + (size_t)(idx / kD) * kMaxFusedP * kPart + 4 + idx % kD;
-#pragma unroll
-      for (int j = 0; j < kMaxFusedP; ++j) x[j] = j < P ? ld_dev(&col[(size_t)j * kPart]) : 0.0f;
-    };
-    load_col(0);
-    for (int g = wave; g < G; g += NW) {
-      const float* pp = pbase + ((size_t)g * kMaxFusedP + lane) * kPart;
-      const float m = lane < P ? ld_dev(&pp[0]) : -INFINITY;
-      const float l = lane < P ? ld_dev(&pp[1]) : 0.0f;
-      const float M = wave_max_dpp(m);
-      const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-      fp[g * kMaxFusedP + lane] = f;
-      const float L = wave_sum_dpp(f * l);
-      if (lane == 0) { mlh[g * 2] = M; mlh[g * 2 + 1] = L; }
+  if constexpr (kTagged) {
+    // ======================================================= mergers
+    // Query head g of the head is merged by block g mod P once all P partials
+    // of g carry this step's tag; a block merges all of its query heads in one
+    // round.  The lanes of wave 0 poll the (m, l) words of one partial each
+    // (lane gi * P + j: partial j of the block's query head gi) and form the
+    // partials' weights against each head's max; then every thread loads one
+    // output dim of every kq-th partial of one head (loading again any word
+    // still unwritten) and the kq sums meet in LDS.  A merger waits at most
+    // as long as a barrier wait may; if that runs out it sets the flags.  A
+    // timeout there or a partial tagged 2 makes the head's outputs NaN (its
+    // partials may rest on an incomplete histogram or incomplete records).
+    // No block waits for the mergers, and no counter orders them.
+    const int ng = sub < G ? (G - 1 - sub) / P + 1 : 0;   // query heads sub, sub + P, ...
+    if (ng > 0) {
+      // ng * P <= 64: one head when P >= G, else P < G <= 8 and ng * P < 2G
+      constexpr int kPerQ = kMaxFusedP / (NT / kD);    // words per thread and head
+      static_assert(kMaxFusedP <= 64 && NT % kD == 0, "merger layout");
+      const int kq = max(1, NT / (ng * kD));            // threads per output
+      float* fpw = reinterpret_cast<float*>(hist);      // [ng * P] partial weights
+      float* hml = fpw + 64;                            // [8][2] heads' max and sum
+      float* red = hml + 16;                            // [ng][kq][kD] partial sums
+      auto part_of = [&](int gi, int j) {
+        return hpart + ((size_t)(sub + gi * P) * kMaxFusedP + j) * kPart;
+      };
+      __syncthreads();
+      if (tid < 64) {
+        const int gi = tid / P, j = tid % P;
+        const bool mine = gi < ng;
+        float m = -INFINITY, l = 0.0f;
+        int bad = 0;
+        if (mine) {
+          const unsigned long long* pp = part_of(gi, j);
+          const unsigned long long t0 = wall_clock64();
+          unsigned long long wm, wl;
+          for (;;) {
+            wm = ld_dev(&pp[0]);
+            wl = ld_dev(&pp[1]);
+            if ((wm >> 32) != 0ull && (wl >> 32) != 0ull) break;
+            if (wall_clock64() - t0 > d.fbar_ticks) { bad = 1; break; }
+            __builtin_amdgcn_s_sleep(2);
+          }
+          if (!bad) {
+            m = __uint_as_float((uint32_t)wm);
+            l = __uint_as_float((uint32_t)wl);
+            bad = ((wm >> 32) | (wl >> 32)) == 2ull ? 2 : 0;
+          }
+        }
+        float myM = -INFINITY;
+        for (int q = 0; q < ng; ++q) {
+          const float Mq = wave_max_dpp(gi == q ? m : -INFINITY);
+          if (gi == q) myM = Mq;
+          if (tid == 0) hml[2 * q] = Mq;
+        }
+        const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - myM);
+        for (int q = 0; q < ng; ++q) {
+          const float Lq = wave_sum_dpp(gi == q ? f * l : 0.0f);
+          if (tid == 0) hml[2 * q + 1] = Lq;
+        }
+        if (mine) fpw[tid] = f;
+        const uint64_t any_late = __ballot(bad == 1), any_tag2 = __ballot(bad == 2);
+        if (tid == 0) S.res[2] = (any_late ? 1 : 0) | (any_tag2 ? 2 : 0);
+        if (tid == 0) S.res[3] = 0;
+      }
+      __syncthreads();
+      int bad = 0;
+      for (int it = tid; it < ng * kq * kD; it += NT) {
+        const int dim = it % kD, q = (it / kD) % kq, gi = it / (kD * kq);
+        const unsigned long long* pp = part_of(gi, 0) + 4 + dim;
+        unsigned long long w[kPerQ];
+  #pragma unroll
+        for (int u = 0; u < kPerQ; ++u) {
+          const int j = q + u * kq;
+          w[u] = j < P ? ld_dev(&pp[(size_t)j * kPart]) : (1ull << 32);
+        }
+        const unsigned long long t0 = wall_clock64();
+        float A = 0.0f;
+  #pragma unroll
+        for (int u = 0; u < kPerQ; ++u) {
+          const int j = q + u * kq;
+          while ((w[u] >> 32) == 0ull && !(bad & 1)) {
+            if (wall_clock64() - t0 > d.fbar_ticks) bad |= 1;
+            __builtin_amdgcn_s_sleep(2);
+            w[u] = ld_dev(&pp[(size_t)j * kPart]);
+          }
+          if ((w[u] >> 32) == 2ull) bad |= 2;
+          if (j < P) A = fmaf(fpw[gi * P + j], __uint_as_float((uint32_t)w[u]), A);
+        }
+        red[it] = A;
+      }
+      if (bad) atomicOr(&S.res[3], bad);
+      __syncthreads();
+      const int flags = S.res[2] | S.res[3];
+      if ((flags & 1) && tid == 0)
+        __hip_atomic_fetch_or(a.ws.fflags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int o = tid; o < ng * kD; o += NT) {
+        const int gi = o / kD, dim = o % kD;
+        float Asum = 0.0f;
+        for (int q = 0; q < kq; ++q) Asum += red[(gi * kq + q) * kD + dim];
+        const float M = hml[2 * gi], L = hml[2 * gi + 1];
+        const size_t bq = (size_t)b * d.Hq + h * G + sub + gi * P;
+        // no rows at all: O = 0, lse = -inf; a NaN sum stays NaN
+        float ov = L != 0.0f ? Asum / L : 0.0f;
+        float ls = L != 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+        if (flags) ov = ls = __builtin_nanf("");
+        a.out[bq * kD + dim] = ov;
+        if (dim == 0 && a.lse) a.lse[bq] = ls;
+      }
+    }
+    if (sub != 0) return;
+    // Block 0 has seen every block's partial of query head 0, so every
+    // block is past both barriers and has read the head's histogram
+    // and counts.
+  } else {
+    wait_mem();
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t old =
+          __hip_atomic_fetch_add(&sync[2 * kSyncStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      S.last = old == (uint32_t)(P - 1);
     }
     __syncthreads();
-#pragma unroll
-    for (int o = 0; o < kOut; ++o) {
-      if (o > 0) load_col(o);
-      const int idx = tid + o * NT;
-      if (idx < G * kD) {
-        const int g = idx / kD, dim = idx % kD;
-        const float* fg = fp + g * kMaxFusedP;
-        float A = 0.0f;
-        // weights and loads are 0 for j >= P
-#pragma unroll
-        for (int j = 0; j < kMaxFusedP; ++j) A = fmaf(fg[j], x[j], A);
-        const float M = mlh[g * 2], L = mlh[g * 2 + 1];
-        const size_t bq = (size_t)b * d.Hq + h * G + g;
-        // no rows at all: O = 0, lse = -inf; a NaN sum stays NaN
-        float o = L != 0.0f ? A / L : 0.0f;
-        float ls = L != 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
-        if (timed_out) o = ls = __builtin_nanf("");
-        a.out[bq * kD + dim] = o;
-        if (dim == 0 && a.lse) a.lse[bq] = ls;
+    if (!S.last) return;
+
+    // ======================================================= last block of the head
+    // every (head, dim) thread loads its column of the P partials (a wave's
+    // loads of one partial are contiguous) while one wave per head loads the
+    // (m, l) pairs and forms the weights of the partials against the head's max.
+    // A head one of whose barrier waits ran out gets NaN instead: its partials
+    // may be built on an incomplete histogram or incomplete records.
+    const bool timed_out = ld_dev(hflag) != 0u;
+    {
+      float* fp = reinterpret_cast<float*>(hist);     // [G][64] weights
+      float* mlh = fp + G * kMaxFusedP;               // [G][2] head max and sum
+      constexpr int kOut = (G * kD + NT - 1) / NT;    // outputs per thread
+      const float* pbase = hpartf;
+      float x[kMaxFusedP];
+      auto load_col = [&](int o) {
+        // threads past the outputs load a valid column and discard it
+        const int idx = min(tid + o * NT, G * kD - 1);
+        const float* col = pbase + (size_t)(idx / kD) * kMaxFusedP * kPart + 4 + idx % kD;
+  #pragma unroll
+        for (int j = 0; j < kMaxFusedP; ++j) x[j] = j < P ? ld_dev(&col[(size_t)j * kPart]) : 0.0f;
+      };
+      load_col(0);
+      for (int g = wave; g < G; g += NW) {
+        const float* pp = pbase + ((size_t)g * kMaxFusedP + lane) * kPart;
+        const float m = lane < P ? ld_dev(&pp[0]) : -INFINITY;
+        const float l = lane < P ? ld_dev(&pp[1]) : 0.0f;
+        const float M = wave_max_dpp(m);
+        const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+        fp[g * kMaxFusedP + lane] = f;
+        const float L = wave_sum_dpp(f * l);
+        if (lane == 0) { mlh[g * 2] = M; mlh[g * 2 + 1] = L; }
+      }
+      __syncthreads();
+  #pragma unroll
+      for (int o = 0; o < kOut; ++o) {
+        if (o > 0) load_col(o);
+        const int idx = tid + o * NT;
+        if (idx < G * kD) {
+          const int g = idx / kD, dim = idx % kD;
+          const float* fg = fp + g * kMaxFusedP;
+          float A = 0.0f;
+          // weights and loads are 0 for j >= P
+  #pragma unroll
+          for (int j = 0; j < kMaxFusedP; ++j) A = fmaf(fg[j], x[j], A);
+          const float M = mlh[g * 2], L = mlh[g * 2 + 1];
+          const size_t bq = (size_t)b * d.Hq + h * G + g;
+          // no rows at all: O = 0, lse = -inf; a NaN sum stays NaN
+          float o = L != 0.0f ? A / L : 0.0f;
+          float ls = L != 0.0f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+          if (timed_out) o = ls = __builtin_nanf("");
+          a.out[bq * kD + dim] = o;
+          if (dim == 0 && a.lse) a.lse[bq] = ls;
+        }
       }
     }
   }
@@ -1235,7 +1412,6 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     for (int i = tc + tid; i < a.max_sel; i += NT) selout[i] = -1;
   }
   if (tid == 0) a.ws.n_rows[bh] = R;
-  // every block of the head is past both barriers and has read the histogram
   for (int i = tid; i < kHistBins; i += NT) st_dev(&ghist[i], 0u);
   if (tid == 0) {
     st_dev(&sync[0], 0u);

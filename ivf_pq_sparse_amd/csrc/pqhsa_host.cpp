@@ -138,7 +138,10 @@ WsLayout ws_layout(const Dims& d, bool dense) {
     l.fsync = o;      o = align_up(o + BH * 3 * kSyncStride * sizeof(uint32_t));
     l.fflags = o;     o = align_up(o + sizeof(uint32_t));
     l.fcnt = o;       o = align_up(o + BH * kMaxFusedP * sizeof(unsigned long long));
-    l.fpart = o;      o = align_up(o + BH * d.G * kMaxFusedP * kPart * sizeof(float));
+    // the fused step's partials: at G = 8 a 64-bit word per value (value and
+    // tag), else a float
+    l.fpart = o;
+    o = align_up(o + BH * d.G * kMaxFusedP * kPart * (d.G == 8 ? sizeof(unsigned long long) : sizeof(float)));
   }
   l.partials = o;     o = align_up(o + (size_t)d.B * d.Hq * d.n_parts * kPart * sizeof(float));
   l.total = o;

@@ -45,7 +45,9 @@ struct WsPtrs {
                        //   finished blocks: each counter on a cache line of its own
   uint32_t* fflags;    // [1] bit 0: a barrier wait timed out
   unsigned long long* fcnt;  // [BH][kMaxFusedP] (above count | tie count << 32) per block
-  float* fpart;        // [BH][G][kMaxFusedP][132] one partial per block and query head
+  unsigned long long* fpart;  // [BH][G][kMaxFusedP][132] one partial per block and query
+                              //   head: at G = 8 64-bit words (float | tag << 32),
+                              //   else floats
 };
 
 // Query reuse: the per-(sequence, query head) rings of earlier queries and
