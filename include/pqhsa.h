@@ -332,7 +332,8 @@ pqhsa_status pqhsa_decode_step_profiled(const pqhsa_shape* shape, const void* in
  * each key as uint16 [B*Hkv][max_context]: the order key's sign, its binary
  * exponent clamped to the 16 binades of [2^-7, 2^9) (the same field range in
  * both halves), then 11 mantissa bits, at least 1 (0 for non-candidates). */
-/* Also: hist (uint32 [B*Hkv][4096] key histogram, hist_bytes long) and
+/* Also: hist (uint32 [B*Hkv][5120]: each (b, h)'s 4096-bin key histogram
+ * followed by 1024 unused words, hist_bytes long) and
  * counters (the fused step's per-head barrier counters and flags, the flags
  * word and per-block counts, counters_bytes long): the regions a step expects
  * to find cleared; total = pqhsa_workspace_bytes. */

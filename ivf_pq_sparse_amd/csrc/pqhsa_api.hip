@@ -359,7 +359,7 @@ pqhsa_status pqhsa_decode_step_noalloc(const pqhsa_shape* shape, const void* ind
   if (!ws) return PQHSA_ERR_HIP;
   // the histogram, counters and flags start at zero: the previous call on
   // this device may have used another shape (another layout of the array)
-  const size_t hist_bytes = (size_t)d.B * d.Hkv * kHistBins * sizeof(uint32_t);
+  const size_t hist_bytes = (size_t)d.B * d.Hkv * kHistStride * sizeof(uint32_t);
   const size_t ctr_bytes = l.fpart - l.fsync;
   const size_t n16 = (hist_bytes + ctr_bytes) / 16;
   const int blocks = (int)std::min<size_t>(1024, (n16 + 255) / 256);
@@ -431,7 +431,7 @@ pqhsa_status pqhsa_step_flags(const pqhsa_shape* shape, void* workspace, size_t 
     // the step's counters, per-head flags, per-block counts and histogram:
     // everything a step expects to find cleared
     PQHSA_TRY(hip_status(hipMemsetAsync(ws + l.hist, 0,
-                                        (size_t)d.B * d.Hkv * kHistBins * sizeof(uint32_t),
+                                        (size_t)d.B * d.Hkv * kHistStride * sizeof(uint32_t),
                                         stream)));
     PQHSA_TRY(hip_status(hipMemsetAsync(ws + l.fsync, 0, l.fpart - l.fsync, stream)));
     PQHSA_TRY(hip_status(hipStreamSynchronize(stream)));

@@ -326,7 +326,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
   unsigned long long* hpart = a.ws.fpart + (size_t)bh * G * kMaxFusedP * kPart;
   float* hpartf = reinterpret_cast<float*>(a.ws.fpart) + (size_t)bh * G * kMaxFusedP * kPart;
   const uint32_t nbar = (uint32_t)(P + d.fbar_extra);   // arrivals a barrier waits for
-  uint32_t* ghist = a.ws.hist + (size_t)bh * kHistBins;
+  uint32_t* ghist = a.ws.hist + (size_t)bh * kHistStride;
   // the top 16 bits of each entry's selection key (0: not a candidate),
   // enough for the 12-bit buckets; a tie's full key is recomputed from its
   // codes when it is recorded

@@ -126,7 +126,7 @@ WsLayout ws_layout(const Dims& d, bool dense) {
     l.qc = o;         o = align_up(o + BH * d.L * d.G * sizeof(float));
     l.keys = o;       o = align_up(o + BH * d.cap * sizeof(uint32_t));
     l.bins = o;       o = align_up(o + BH * d.L * d.G * 2 * sizeof(float));
-    l.hist = o;       o = align_up(o + BH * kHistBins * sizeof(uint32_t));
+    l.hist = o;       o = align_up(o + BH * kHistStride * sizeof(uint32_t));
     l.seg_above = o;  o = align_up(o + BH * d.cap * 2 * sizeof(int32_t));
     l.seg_aw = o;     o = align_up(o + BH * d.cap * d.G * sizeof(float));
     l.seg_tie = o;    o = align_up(o + BH * d.cap * 4 * sizeof(uint32_t));
@@ -247,7 +247,7 @@ pqhsa_status pqhsa_workspace_layout(const pqhsa_shape* shape, int dense, pqhsa_w
   out->n_bg_splits = d.n_bg_splits;
   out->n_parts = d.n_parts;
   out->hist = l.hist;
-  out->hist_bytes = dense ? 0 : (size_t)d.B * d.Hkv * kHistBins * sizeof(uint32_t);
+  out->hist_bytes = dense ? 0 : (size_t)d.B * d.Hkv * kHistStride * sizeof(uint32_t);
   out->counters = l.fsync;
   out->counters_bytes = dense ? 0 : l.fpart - l.fsync;
   out->total = l.total;

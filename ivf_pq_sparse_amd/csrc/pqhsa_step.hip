@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void k_tables(StepArgs a) {
   {
     const int nb = gridDim.y;
     for (int i = blockIdx.y * blockDim.x + threadIdx.x; i < kHistBins; i += nb * blockDim.x)
-      a.ws.hist[(size_t)bh * kHistBins + i] = 0;
+      a.ws.hist[(size_t)bh * kHistStride + i] = 0;
   }
   if (blockIdx.y < kM) {
     const int m = blockIdx.y;
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(StepArgs a) {
   }
   (void)cur;
   __syncthreads();
-  uint32_t* gh = a.ws.hist + (size_t)bh * kHistBins;
+  uint32_t* gh = a.ws.hist + (size_t)bh * kHistStride;
   for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) {
     const uint32_t v = hist[i];
     if (v) atomicAdd(&gh[i], v);
@@ -567,7 +567,7 @@ __device__ void select_head(const StepArgs& a, int bh, const SeqInfo& si, unsign
   if (tid == 0) a.ws.n_rows[bh] = base_r + (si.T - rb);
   // every collect block has read the histogram: leave it cleared (the fused
   // step expects a zero histogram)
-  for (int i = tid; i < kHistBins; i += nthr) a.ws.hist[(size_t)bh * kHistBins + i] = 0u;
+  for (int i = tid; i < kHistBins; i += nthr) a.ws.hist[(size_t)bh * kHistStride + i] = 0u;
   if (wsel_lds) {
     unsigned long long* out = a.ws.wsel + (size_t)bh * nwsel;
     for (int i = tid; i < nwsel; i += nthr) out[i] = wacc[i];
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(kCollectThreads) void k_collect(StepArgs a) {
       kv[j] = e < e1 ? keys[e] : 0u;
     }
     int beta, above, total;
-    find_threshold(a.ws.hist + (size_t)bh * kHistBins, si.k, L.sh, &beta, &above, &total);
+    find_threshold(a.ws.hist + (size_t)bh * kHistStride, si.k, L.sh, &beta, &above, &total);
     // per-thread counts, block exclusive scan, then in-order placement
     int ca = 0, ct = 0;
 #pragma unroll
