@@ -1263,14 +1263,14 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
         const int dim = it % kD, q = (it / kD) % kq, gi = it / (kD * kq);
         const unsigned long long* pp = part_of(gi, 0) + 4 + dim;
         unsigned long long w[kPerQ];
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < kPerQ; ++u) {
           const int j = q + u * kq;
           w[u] = j < P ? ld_dev(&pp[(size_t)j * kPart]) : (1ull << 32);
         }
         const unsigned long long t0 = wall_clock64();
         float A = 0.0f;
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < kPerQ; ++u) {
           const int j = q + u * kq;
           while ((w[u] >> 32) == 0ull && !(bad & 1)) {
@@ -1334,7 +1334,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
         // threads past the outputs load a valid column and discard it
         const int idx = min(tid + o * NT, G * kD - 1);
         const float* col = pbase + (size_t)(idx / kD) * kMaxFusedP * kPart + 4 + idx % kD;
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < kMaxFusedP; ++j) x[j] = j < P ? ld_dev(&col[(size_t)j * kPart]) : 0.0f;
       };
       load_col(0);
@@ -1349,7 +1349,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
         if (lane == 0) { mlh[g * 2] = M; mlh[g * 2 + 1] = L; }
       }
       __syncthreads();
-  #pragma unroll
+#pragma unroll
       for (int o = 0; o < kOut; ++o) {
         if (o > 0) load_col(o);
         const int idx = tid + o * NT;
@@ -1358,7 +1358,7 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
           const float* fg = fp + g * kMaxFusedP;
           float A = 0.0f;
           // weights and loads are 0 for j >= P
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < kMaxFusedP; ++j) A = fmaf(fg[j], x[j], A);
           const float M = mlh[g * 2], L = mlh[g * 2 + 1];
           const size_t bq = (size_t)b * d.Hq + h * G + g;
