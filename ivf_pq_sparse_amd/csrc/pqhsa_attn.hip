@@ -442,8 +442,30 @@ __global__ __launch_bounds__(128 * NG) void k_merge(StepArgs a) {
   float* wts = mlds;
   float* ls = mlds + np;
   float* gsum = mlds + 2 * np;
+  // this thread's output dim of its group's first kPre partials is loaded
+  // right after the (m, l) pairs, before anything waits on them, so that
+  // the merge takes one round of loads (two where a group has more)
+  constexpr int kPre = 32;
+  const int dim = tid & (kD - 1), grp = tid >> 7;
+  const int hp = (np + NG - 1) / NG;
+  const int i0 = grp * hp, i1 = min(np, i0 + hp);
+  const float* pd = part + 4 + dim;
+  float mv = -INFINITY, lv = 0.0f;
+  const bool has_ml = tid < np;
+  if (has_ml) {
+    mv = part[(size_t)tid * kPart];
+    lv = part[(size_t)tid * kPart + 1];
+  }
+  float xp[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) xp[u] = (i0 + u < i1) ? pd[(size_t)(i0 + u) * kPart] : 0.0f;
   float mx = -INFINITY;
-  for (int i = tid; i < np; i += blockDim.x) {
+  if (has_ml) {
+    wts[tid] = mv;
+    ls[tid] = lv;
+    mx = mv;
+  }
+  for (int i = tid + blockDim.x; i < np; i += blockDim.x) {
     const float m = part[(size_t)i * kPart];
     wts[i] = m;
     ls[i] = part[(size_t)i * kPart + 1];
@@ -475,12 +497,11 @@ __global__ __launch_bounds__(128 * NG) void k_merge(StepArgs a) {
 #pragma unroll
     for (int w = 0; w < n / 2; ++w) t[w] = t[2 * w] + t[2 * w + 1];
   const float L = t[0];
-  const int dim = tid & (kD - 1), grp = tid >> 7;
-  const int hp = (np + NG - 1) / NG;
-  const int i0 = grp * hp, i1 = min(np, i0 + hp);
-  const float* pd = part + 4 + dim;
   float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int i = i0; i < i1; i += 16) {
+#pragma unroll
+  for (int u = 0; u < kPre; ++u)
+    if (i0 + u < i1) A[u & 3] = fmaf(wts[i0 + u], xp[u], A[u & 3]);
+  for (int i = i0 + kPre; i < i1; i += 16) {
     float x[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) x[u] = (i + u < i1) ? pd[(size_t)(i + u) * kPart] : 0.0f;
