@@ -1207,6 +1207,13 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     // partials may rest on an incomplete histogram or incomplete records).
     // No block waits for the mergers, and no counter orders them.
     const int ng = sub < G ? (G - 1 - sub) / P + 1 : 0;   // query heads sub, sub + P, ...
+    if (sub == 0) {
+      // every block is past both barriers' arrivals and has read the
+      // histogram and the first counter; the second is cleared at the end
+      // (a block may still be polling it)
+      for (int i = tid; i < kHistBins; i += NT) st_dev(&ghist[i], 0u);
+      if (tid == 0) st_dev(&sync[0], 0u);
+    }
     if (ng > 0) {
       // ng * P <= 64: one head when P >= G, else P < G <= 8 and ng * P < 2G
       constexpr int kPerQ = kMaxFusedP / (NT / kD);    // words per thread and head
@@ -1337,16 +1344,30 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
 #pragma unroll
         for (int j = 0; j < kMaxFusedP; ++j) x[j] = j < P ? ld_dev(&col[(size_t)j * kPart]) : 0.0f;
       };
+      // wave g loads the (m, l) pairs of query head g, then every thread its
+      // column, and then the head's histogram and counters are cleared (every
+      // block is past both barriers and done with them): the clears are
+      // issued after the loads, so waiting for the loads never waits for them
+      static_assert(G <= NW && kOut == 1, "one wave per head, one output per thread");
+      float m = -INFINITY, l = 0.0f;
+      if (wave < G && lane < P) {
+        const float* pp = pbase + ((size_t)wave * kMaxFusedP + lane) * kPart;
+        m = ld_dev(&pp[0]);
+        l = ld_dev(&pp[1]);
+      }
       load_col(0);
-      for (int g = wave; g < G; g += NW) {
-        const float* pp = pbase + ((size_t)g * kMaxFusedP + lane) * kPart;
-        const float m = lane < P ? ld_dev(&pp[0]) : -INFINITY;
-        const float l = lane < P ? ld_dev(&pp[1]) : 0.0f;
+      for (int i = tid; i < kHistBins; i += NT) st_dev(&ghist[i], 0u);
+      if (tid == 0) {
+        st_dev(&sync[0], 0u);
+        st_dev(&sync[kSyncStride], 0u);
+        st_dev(&sync[2 * kSyncStride], 0u);
+      }
+      if (wave < G) {
         const float M = wave_max_dpp(m);
         const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-        fp[g * kMaxFusedP + lane] = f;
+        fp[wave * kMaxFusedP + lane] = f;
         const float L = wave_sum_dpp(f * l);
-        if (lane == 0) { mlh[g * 2] = M; mlh[g * 2 + 1] = L; }
+        if (lane == 0) { mlh[wave * 2] = M; mlh[wave * 2 + 1] = L; }
       }
       __syncthreads();
 #pragma unroll
@@ -1411,10 +1432,9 @@ __global__ __launch_bounds__(FusedCfg<G>::NT) void k_fused(StepArgs a) {
     }
     for (int i = tc + tid; i < a.max_sel; i += NT) selout[i] = -1;
   }
-  if (tid == 0) a.ws.n_rows[bh] = R;
-  for (int i = tid; i < kHistBins; i += NT) st_dev(&ghist[i], 0u);
   if (tid == 0) {
-    st_dev(&sync[0], 0u);
+    a.ws.n_rows[bh] = R;
+    // the histogram and the other counters were cleared above
     st_dev(&sync[kSyncStride], 0u);
     st_dev(&sync[2 * kSyncStride], 0u);
     st_dev(hflag, 0u);
