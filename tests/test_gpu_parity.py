@@ -457,15 +457,18 @@ def test_poisoned_workspace_parity(staged):
     parity(inp, what="ragged batch", staged=staged, poison=True, page_seed=6)
 
 
-def test_barrier_timeout_is_reported_and_cleared():
+@pytest.mark.parametrize("G", [4, 8])
+def test_barrier_timeout_is_reported_and_cleared(G):
     # The barrier test variant waits for one block more than the grid has and
     # gives up after 20 us, so every wait runs out while every kernel still
     # ends normally: the call returns, the flag is set and every output is
-    # NaN.  After the flag is read and the workspace cleared, the next step
-    # matches the oracle.
+    # NaN (at G = 8 through the tagged partials' timeout tag, elsewhere
+    # through the head's flag).  After the flag is read and the workspace
+    # cleared, the next step matches the oracle.
     import ivf_pq_sparse_amd as pq
     from pqhsa_synth.device import stage
-    inp = make_step_inputs(1)
+    inp = make_step_inputs(1) if G == 4 else make_step_inputs(
+        1, num_q_heads=32, num_kv_heads=4, workload_id=62)
     tens, kw = stage(inp, "cuda")
     shape = pq.make_shape(**kw)
     dec = pq.PQHSADecoder(shape)
