@@ -28,6 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+GATHER_ROWS = 1 << 21          # the gather calibration: rows picked at random
+GATHER_ROW_BYTES = 256
 METRIC = "µs/decode step/layer @128K, 1% budget; HBM GB/s vs peak; × vs dense split-K"
 
 
@@ -162,6 +164,7 @@ def summarize_profile(trace_dir, fetch_dir, write_dir, out, command):
     stats = rows(trace_dir, "*kernel_stats.csv")
     counters = {}
     copy_kib = {}
+    gather_kib = {}
     for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         per = {}
         for r in rows(d, "*counter_collection.csv"):
@@ -170,6 +173,8 @@ def summarize_profile(trace_dir, fetch_dir, write_dir, out, command):
             v = float(r["Counter_Value"])
             if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer"):
                 copy_kib[cname] = max(copy_kib.get(cname, 0.0), v)
+            if "vectorized_gather_kernel" in r["Kernel_Name"]:
+                gather_kib[cname] = max(gather_kib.get(cname, 0.0), v)
             per.setdefault(_short_kernel(r["Kernel_Name"]), []).append(v)
         counters[cname] = {k: (float(np.mean(v)), len(v)) for k, v in per.items()}
     gib_kib = float(1 << 20)
@@ -184,6 +189,15 @@ def summarize_profile(trace_dir, fetch_dir, write_dir, out, command):
         if c in copy_kib:
             lines.append(f"- {c}: {copy_kib[c]:.1f} KiB counted for {gib_kib:.0f} KiB moved: "
                          f"scale x{scale[c]:.4f}")
+    if gather_kib:
+        g_read = GATHER_ROWS * (GATHER_ROW_BYTES + 8) / 1024.0
+        g_write = GATHER_ROWS * GATHER_ROW_BYTES / 1024.0
+        lines += ["", f"Gather check (largest `vectorized_gather_kernel` dispatch, torch's index_select: {GATHER_ROWS} random rows of "
+                  f"{GATHER_ROW_BYTES} B and their 8 B indices read, the rows written):", ""]
+        for c, moved in (("FETCH_SIZE", g_read), ("WRITE_SIZE", g_write)):
+            if c in gather_kib:
+                lines.append(f"- {c}: {gather_kib[c]:.1f} KiB counted for {moved:.0f} KiB moved: "
+                             f"scale x{moved / gather_kib[c]:.4f}")
     lines += ["", "| kernel | calls | avg ns | min ns | max ns | FETCH KiB/dispatch | "
               "WRITE KiB/dispatch | scaled MB/dispatch (read + write) |",
               "|---|---|---|---|---|---|---|---|"]
@@ -779,6 +793,16 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copy calibration: {n * 4} bytes read and written")
+        # and a gather of known bytes: 2M random rows of 256 B (the step's K/V
+        # rows are 256 B runs) and their 8-byte indices read, the rows written
+        rows = src.view(-1, GATHER_ROW_BYTES // 4)
+        g = torch.Generator(device="cuda").manual_seed(7)
+        idx = torch.randperm(rows.shape[0], device="cuda", generator=g)[:GATHER_ROWS]
+        torch.cuda.synchronize()
+        picked = rows.index_select(0, idx)
+        torch.cuda.synchronize()
+        log(f"gather calibration: {picked.numel() * 4} bytes of rows gathered")
+        del picked, idx
 
     # dominant kernel (longest average duration) and its roofline over its
     # algorithmic bytes (for the fused kernel, the whole step's: codes, list

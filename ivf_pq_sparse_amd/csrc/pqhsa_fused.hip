@@ -49,8 +49,10 @@
 // launch would guarantee the same but costs tens of µs per launch.)  If CUs
 // are withheld, waits are bounded in time: a wait that runs out sets bit 0 of
 // the workspace flags and the head's own flag, and the step goes on, so a call
-// always finishes; the head's last block then writes NaN to the head's outputs
-// instead of a result.  Counts read across blocks are clamped to each block's
+// always finishes; the head's outputs are then NaN instead of a result (the
+// last block reads the head's flag; at G = 8 the mergers see the timeout in
+// the partials' tags, and a merger whose own wait for the partials runs out
+// sets the flag too).  Counts read across blocks are clamped to each block's
 // own entry range, so that whatever a late block left behind, every access
 // stays inside its array.
 #include "pqhsa_internal.hpp"
