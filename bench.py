@@ -60,7 +60,7 @@ def parse():
     p.add_argument("--no-graph", action="store_true",
                    help="skip the graph-replayed timing (profiled runs)")
     p.add_argument("--no-other-workloads", action="store_true",
-                   help="skip the 32K, 16 x 128K and 512K lines beside the main workload")
+                   help="skip the 8K, 32K, 16 x 128K and 512K lines beside the main workload")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain device copy of known size (for counter scaling)")
     p.add_argument("--sweep", choices=["configs", "budget", "context", "append", "reuse"],
@@ -358,7 +358,7 @@ class Rig:
 
 
 def other_workloads(main_wid, steps=128, warmup=64):
-    """The 32K, 16 x 128K and 512K workloads beside the main one: PQ-HSA and
+    """The 8K, 32K, 16 x 128K and 512K workloads beside the main one: PQ-HSA and
     dense split-K µs per step on rotated layer copies, the speed-up and the
     step's algorithmic bytes and rate."""
     import torch
@@ -366,7 +366,7 @@ def other_workloads(main_wid, steps=128, warmup=64):
     import ivf_pq_sparse_amd as pq
     from pqhsa_synth import WORKLOADS, make_step_inputs
     out = {}
-    for wid in (1, 3, 4):
+    for wid in (0, 1, 3, 4):
         if wid == main_wid:
             continue
         w = WORKLOADS[wid]
